@@ -1,0 +1,297 @@
+#!/usr/bin/env python3
+"""Throughput of the fused sparse MoE layer on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode]
+
+A step is one pass of the whole layer (route, align, gate/up GEMM + SiLU*mul,
+down GEMM, combine: the five C-ABI calls) over one batch of synthetic
+inputs already resident in HBM. W untimed steps, then exactly K timed steps
+between two device synchronisations; the weights are rotated over
+``--copies`` resident copies so the 256 MB Infinity Cache cannot serve one
+step's weights to the next. HIP events recorded on the launch stream around
+every call inside the timed region give each kernel's average duration; the
+dominant kernel's algorithmic bytes (or flops) per launch over that duration
+is the roofline entry. The CPU oracle is timed on a bounded sample of the
+same workload on the host cores (cpu_baseline).
+
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+METRIC = "MoE-layer tokens/s; achieved HBM GB/s (decode) and MFMA TFLOP/s (prefill)"
+WORKLOAD_TEXT = {
+    "tiny": "tiny MoE layer",
+    "decode": "decode-shaped Qwen3-MoE layer",
+    "prefill": "prefill-shaped Qwen3-MoE layer",
+    "skewed": "skewed-routing (Zipf 1.2) MoE layer",
+    "large": "large MoE layer on one GPU",
+}
+KERNELS = ["route", "align", "gate_up", "down", "combine"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = {
+    "gate_up": ["gemm.hip", "moe_common.h"],
+    "down": ["gemm.hip", "moe_common.h"],
+    "route": ["route.hip", "moe_common.h"],
+    "align": ["align.hip"],
+    "combine": ["combine.hip", "moe_common.h"],
+}
+
+
+def progress(msg: str):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def source_hash(kernel: str) -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, "sparse_mixture_experts_softmax_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str, kernel: str):
+    """HBM bytes per launch from the committed counter runs, or None when
+    absent or taken on a different version of the kernel's source."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            rec = json.load(fh).get(f"{workload}/{kernel}")
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_sha") != source_hash(kernel):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def algorithmic_work(shape, counts):
+    """Per-kernel algorithmic bytes and flops for one step (each touched
+    expert's weights read once; activations, router weights and outputs read
+    or written once; padding, re-reads and intermediates' round trips are
+    not counted)."""
+    T, H, E, k, I = shape.T, shape.H, shape.E, shape.k, shape.I
+    touched = int((counts > 0).sum())
+    pairs = T * k
+    b = 2  # bf16
+    return {
+        "route": {"bytes": T * H * b + E * H * b + T * E * 4 + pairs * 8, "flops": 2 * T * H * E},
+        "align": {"bytes": pairs * 4 * 2, "flops": 0},
+        "gate_up": {"bytes": touched * 2 * I * H * b + T * H * b + pairs * I * b, "flops": 2 * pairs * 2 * I * H},
+        "down": {"bytes": touched * H * I * b + pairs * I * b + pairs * H * b, "flops": 2 * pairs * H * I},
+        "combine": {"bytes": pairs * H * b + pairs * 4 + T * H * b, "flops": 2 * pairs * H},
+        "layer": {"bytes": touched * 3 * I * H * b + E * H * b + 2 * T * H * b,
+                  "flops": 2 * pairs * 3 * H * I + 2 * T * H * E},
+        "touched_experts": touched,
+    }
+
+
+def cpu_baseline(inp, seconds: float):
+    """Oracle tokens/s on the host cores over a bounded sample of the same
+    workload: the whole batch repeated, or a prefix of it, for about
+    `seconds` of CPU work."""
+    import numpy as np
+
+    import oracle
+
+    s = inp.shape
+    orc = oracle.default()
+    n = min(s.T, 8)
+    t0 = time.perf_counter()
+    orc.moe_layer(inp.x, inp.w_router, inp.w13, inp.w2, s.k, s.norm_topk_prob, inp.router_bias, np.arange(n))
+    per_token = (time.perf_counter() - t0) / n
+    budget_tokens = max(1, int(seconds / max(per_token, 1e-9)))
+    if budget_tokens >= s.T:
+        reps = max(1, budget_tokens // s.T)
+        tokens = np.arange(s.T)
+        sample = f"whole batch of {s.T} tokens x {reps} repeats"
+    else:
+        reps = 1
+        tokens = np.arange(budget_tokens)
+        sample = f"first {budget_tokens} of {s.T} tokens"
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        orc.moe_layer(inp.x, inp.w_router, inp.w13, inp.w2, s.k, s.norm_topk_prob, inp.router_bias, tokens)
+    dt = time.perf_counter() - t0
+    return {
+        "value": round(len(tokens) * reps / dt, 3),
+        "unit": "tokens/s",
+        "cores": orc.max_threads(),
+        "kind": "oracle",
+        "sample": f"{sample}; float64 per-token loop, {dt:.1f} s",
+    }
+
+
+def copy_calibration(mb: int):
+    """A plain device-to-device copy of `mb` MiB, for scaling HBM counters."""
+    import torch
+
+    n = mb * 1024 * 1024
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n, "launches": 3}))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="decode", choices=list(WORKLOAD_TEXT))
+    ap.add_argument("--copies", type=int, default=0, help="resident weight copies rotated over steps (0 = auto)")
+    ap.add_argument("--block-m", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU-baseline budget; 0 skips it")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--copy-calibration-mb", type=int, default=0)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synth
+    import sparse_mixture_experts_softmax_amd as moe
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    moe.lib()  # fail loudly if the HIP library is not built
+    if args.copy_calibration_mb:
+        copy_calibration(args.copy_calibration_mb)
+        return
+
+    shape = synth.CONFIGS[args.workload]
+    progress(f"generating {args.workload} inputs (T={shape.T} H={shape.H} E={shape.E} k={shape.k} I={shape.I})")
+    inp = synth.make_inputs(shape, seed=args.seed)
+    T, H, E, k, I = shape.T, shape.H, shape.E, shape.k, shape.I
+    weight_bytes = (inp.w13.nbytes + inp.w2.nbytes)
+    copies = args.copies or max(1, min(4, -(-(512 << 20) // weight_bytes) + 1))
+
+    def dev(bits):
+        return torch.from_numpy(bits).view(torch.bfloat16).to("cuda")
+
+    x = dev(inp.x)
+    wr = dev(inp.w_router)
+    bias = None if inp.router_bias is None else torch.from_numpy(inp.router_bias).cuda()
+    w13s = [dev(inp.w13)]
+    w2s = [dev(inp.w2)]
+    for _ in range(copies - 1):
+        w13s.append(w13s[0].clone())
+        w2s.append(w2s[0].clone())
+    block_m = args.block_m or moe.moe_pick_block_m(T, k, E)
+    b = moe.allocate(T, H, E, k, I, "cuda", block_m)
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+
+    def step(c, ev=None):
+        w13, w2 = w13s[c % copies], w2s[c % copies]
+        if ev:
+            ev[0].record(stream)
+        moe.moe_route(x, wr, bias, b.logits, b.topk_ids, b.topk_weights, T, H, E, k, shape.norm_topk_prob, sp)
+        if ev:
+            ev[1].record(stream)
+        moe.moe_align_by_expert(b.topk_ids, T, k, E, block_m, b.sorted_ids, b.block_expert, b.expert_counts,
+                                b.num_padded, b.workspace, sp)
+        if ev:
+            ev[2].record(stream)
+        moe.moe_grouped_gemm_gate_up_silu(x, w13, b.sorted_ids, b.block_expert, b.num_padded, T, k, H, I, E, block_m,
+                                          b.cap, b.act, sp)
+        if ev:
+            ev[3].record(stream)
+        moe.moe_grouped_gemm_down(b.act, w2, b.sorted_ids, b.block_expert, b.num_padded, T, k, H, I, E, block_m,
+                                  b.cap, b.y, sp)
+        if ev:
+            ev[4].record(stream)
+        moe.moe_combine(b.y, b.topk_weights, T, k, H, b.out, sp)
+        if ev:
+            ev[5].record(stream)
+
+    progress(f"warmup {args.warmup} steps (block_m={block_m}, {copies} weight copies)")
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    progress(f"timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, events[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    per_kernel_ms = {name: float(np.mean([ev[j].elapsed_time(ev[j + 1]) for ev in events]))
+                     for j, name in enumerate(KERNELS)}
+    ms_per_step = elapsed * 1e3 / args.steps
+    counts = b.expert_counts.cpu().numpy()
+    work = algorithmic_work(shape, counts)
+
+    bound = "hbm" if args.workload in ("decode", "tiny") else "mfma"
+    dom = "gate_up"
+    dom_s = per_kernel_ms[dom] * 1e-3
+    if bound == "hbm":
+        achieved = work[dom]["bytes"] / dom_s / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBPS, 4)}
+    else:
+        achieved = work[dom]["flops"] / dom_s / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4)}
+    roof["kernel"] = "grouped_gemm_kernel<gate_up> (moe_grouped_gemm_gate_up_silu)"
+    roof["kernel_ms"] = round(per_kernel_ms[dom], 5)
+    roof["algorithmic_per_launch"] = work[dom]["bytes"] if bound == "hbm" else work[dom]["flops"]
+    roof["traffic"] = measured_traffic(args.workload, dom)
+
+    layer_s = ms_per_step * 1e-3
+    result = {
+        "metric": METRIC,
+        "value": round(T / layer_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) activations, N(0,0.02) weights, bf16)",
+        "config": {"workload": WORKLOAD_TEXT[args.workload], "T": T, "hidden": H, "experts": E, "top_k": k,
+                   "intermediate": I, "norm_topk_prob": shape.norm_topk_prob, "block_m": block_m,
+                   "weight_copies_rotated": copies, "touched_experts": work["touched_experts"]},
+        "roofline": roof,
+        "layer": {
+            "hbm_GBps": round(work["layer"]["bytes"] / layer_s / 1e9, 1),
+            "hbm_frac": round(work["layer"]["bytes"] / layer_s / 1e9 / PEAK_HBM_GBPS, 4),
+            "mfma_TFLOPs": round(work["layer"]["flops"] / layer_s / 1e12, 2),
+            "mfma_frac": round(work["layer"]["flops"] / layer_s / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "kernel_ms": {n: round(v, 5) for n, v in per_kernel_ms.items()},
+        },
+    }
+    if args.cpu_seconds > 0:
+        progress(f"CPU baseline (oracle, ~{args.cpu_seconds:.0f} s)")
+        result["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
+    else:
+        result["cpu_baseline"] = None
+    props = torch.cuda.get_device_properties(0)
+    result["device"] = {"name": props.name, "cus": props.multi_processor_count,
+                        "arch": getattr(props, "gcnArchName", "")}
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

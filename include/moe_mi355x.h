@@ -1,0 +1,196 @@
+/*
+ * moe_mi355x.h -- C ABI of the fused sparse Mixture-of-Experts layer for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The layer, as the pages define it:
+ *   [MoE]     mini-sglang guide, chapter 7 (models, MoE backend, kernel
+ *             infrastructure), paragraph on the MoE routing layer: a router
+ *             linear gives per-expert logits, the top-k experts are chosen
+ *             as torch.topk does, and the k expert outputs are weighted by
+ *             their softmax scores and summed; paragraph on the fused
+ *             backend: tokens are grouped by their assigned expert so each
+ *             expert's weights are read with coalesced accesses.
+ *   [Linear]  handbook page "The op layer: BaseOP and the layers", section
+ *             "Linear layers": a linear layer is y = x W^T (+ b); the MoE
+ *             router is replicated, not sharded.
+ *   [Models]  handbook page "Models and weight loading": section
+ *             "ModelConfig" (num_experts, num_experts_per_tok,
+ *             moe_intermediate_size, norm_topk_prob), section "Model
+ *             structure" (each expert is a GatedMLP: merged gate_up
+ *             projection, silu(gate) * up, down projection; only silu) and
+ *             section "Streaming weight loading" (per-expert weights stacked
+ *             into [E, ...]; gate and up merged in that order).
+ *
+ * The layer is five calls, in this order, on one stream:
+ *   moe_route -> moe_align_by_expert -> moe_grouped_gemm_gate_up_silu ->
+ *   moe_grouped_gemm_down -> moe_combine
+ * No residual is added (the decoder adds it outside the MLP).
+ *
+ * Conventions for every call
+ *  - Pointers named as device pointers must point to device memory of the
+ *    current HIP device; the caller allocates and owns every buffer. The
+ *    library allocates nothing, frees nothing and keeps no pointer after the
+ *    call returns.
+ *  - All tensors are dense and row-major. bf16 tensors are passed as void*
+ *    holding raw bfloat16 bit patterns; fp32 as float*; indices as int32_t*.
+ *  - `stream` is a hipStream_t (NULL = the default stream). Every call only
+ *    enqueues work: it never synchronises and never reads device memory on
+ *    the host. Arguments are validated on the host before anything is
+ *    enqueued; a call that fails validation enqueues nothing.
+ *  - Return value: MOE_OK, or a negative MOE_ERR_* code. moe_last_error()
+ *    returns a thread-local message describing the last failure.
+ *  - Limits: 1 <= E <= 256, 1 <= k <= min(E, 32), H % 64 == 0, I % 32 == 0,
+ *    T >= 0 (T == 0 is a successful no-op), T * k < 2^31,
+ *    block_m in {16, 32, 64, 128}.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+#define MOE_OK 0
+#define MOE_ERR_INVALID (-1)     /* null required pointer, negative size, bad enum */
+#define MOE_ERR_UNSUPPORTED (-2) /* shape outside the limits above */
+#define MOE_ERR_HIP (-3)         /* HIP launch/configuration error */
+#define MOE_ERR_WORKSPACE (-4)   /* workspace or capacity too small */
+
+#define MOE_OUT_BF16 0
+#define MOE_OUT_FP32 1
+
+/* Version of this ABI (MOE_ABI_VERSION). */
+int moe_abi_version(void);
+
+/* Message for the last failing call on this thread ("" if none). The string
+ * is owned by the library and valid until the next call on this thread. */
+const char* moe_last_error(void);
+
+/*
+ * Router linear, softmax, top-k and optional renormalisation ([MoE],
+ * [Linear], [Models] norm_topk_prob).
+ *
+ *   x            [T, H] bf16, device. May be NULL: then `logits` is an input.
+ *   w_router     [E, H] bf16, device (ignored when x is NULL).
+ *   router_bias  [E] fp32, device, or NULL for no bias (ignored when x is NULL).
+ *   logits       [T, E] fp32, device. Output when x != NULL:
+ *                logits[t,e] = sum_h x[t,h] * w_router[e,h] + bias[e],
+ *                accumulated in fp32. Input when x == NULL.
+ *   topk_ids     [T, k] int32, device, output: the k experts with the largest
+ *                logits (equivalently the largest softmax scores), in
+ *                descending order; equal logits -> lower expert index first.
+ *   topk_weights [T, k] fp32, device, output: softmax over all E experts at
+ *                the selected experts; if norm_topk_prob != 0, divided by
+ *                their sum over the k selected experts (then they sum to 1).
+ * Selection is decided on the fp32 logits, so given the same logits it is
+ * exact and reproducible.
+ */
+int moe_route(const void* x, const void* w_router, const float* router_bias, float* logits, int32_t* topk_ids,
+              float* topk_weights, int64_t T, int32_t H, int32_t E, int32_t k, int32_t norm_topk_prob,
+              void* stream);
+
+/*
+ * Rows of the expert-grouped permutation sufficient for any routing of T
+ * tokens: T*k real rows plus at most block_m-1 pad rows for each non-empty
+ * expert, rounded up to block_m. Returns -1 on invalid arguments.
+ */
+int64_t moe_align_capacity(int64_t T, int32_t k, int32_t E, int32_t block_m);
+
+/* Bytes of device workspace moe_align_by_expert needs (per-tile expert
+ * histograms). Returns 0 when none is needed or the arguments are invalid. */
+size_t moe_align_workspace_bytes(int64_t T, int32_t k, int32_t E, int32_t block_m);
+
+/*
+ * Group (token, slot) pairs by assigned expert ([MoE], fused-backend
+ * paragraph), padded to the GEMM row tile.
+ *
+ *   topk_ids      [T, k] int32, device, input (values in [0, E)).
+ *   cap           = moe_align_capacity(T, k, E, block_m) rows (not passed:
+ *                   the output buffers must have at least these sizes).
+ *   sorted_ids    [cap] int32, device, output. The flat index i = t*k + j of
+ *                 slot j of token t. Expert e owns rows
+ *                 [off_e, off_e + pad_e), pad_e = ceil(c_e/block_m)*block_m,
+ *                 c_e = number of pairs routed to e, off_e = sum of pad_e'
+ *                 for e' < e. Its first c_e rows hold its flat indices in
+ *                 ascending order; its other rows, and every row from
+ *                 num_padded on, hold the sentinel T*k.
+ *   block_expert  [cap / block_m] int32, device, output: owner expert of
+ *                 each block_m-row block, -1 for blocks from num_padded on.
+ *                 Experts with no pairs own no block.
+ *   expert_counts [E] int32, device, output: c_e.
+ *   num_padded    [1] int32, device, output: sum of pad_e.
+ *   workspace     device scratch of at least moe_align_workspace_bytes(...)
+ *                 bytes (may be NULL when that is 0); contents on entry are
+ *                 ignored.
+ * The result is deterministic (no order-dependent atomics).
+ */
+int moe_align_by_expert(const int32_t* topk_ids, int64_t T, int32_t k, int32_t E, int32_t block_m,
+                        int32_t* sorted_ids, int32_t* block_expert, int32_t* expert_counts, int32_t* num_padded,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Grouped gate/up projection with fused SiLU-and-mul ([Models], "Model
+ * structure": gate_up_proj, then silu(gate) * up). For every row r below
+ * num_padded whose sorted_ids[r] = i is not the sentinel, with token
+ * t = i / k and expert e = block_expert[r / block_m]:
+ *   g_c = sum_h x[t,h] * w13[e, c, h],  u_c = sum_h x[t,h] * w13[e, I + c, h]
+ *   act[r, c] = bf16(silu(g_c) * u_c),  silu(z) = z / (1 + exp(-z)),
+ * with bf16 products accumulated in fp32 on the matrix cores. Pad rows are
+ * written as zeros. Rows from num_padded on are not touched.
+ *
+ *   x          [T, H] bf16, device.
+ *   w13        [E, 2I, H] bf16, device: rows 0..I-1 gate, I..2I-1 up.
+ *   sorted_ids, block_expert, num_padded: from moe_align_by_expert with the
+ *              same T, k, E, block_m; cap = moe_align_capacity(...).
+ *   act        [cap, I] bf16, device, output (rows in sorted order).
+ */
+int moe_grouped_gemm_gate_up_silu(const void* x, const void* w13, const int32_t* sorted_ids,
+                                  const int32_t* block_expert, const int32_t* num_padded, int64_t T, int32_t k,
+                                  int32_t H, int32_t I, int32_t E, int32_t block_m, int64_t cap, void* act,
+                                  void* stream);
+
+/*
+ * Grouped down projection ([Models], "Model structure": down_proj). For
+ * every row r below num_padded with sorted_ids[r] = i not the sentinel and
+ * e = block_expert[r / block_m]:
+ *   y[i, h] = bf16(sum_c act[r, c] * w2[e, h, c])
+ * (fp32 accumulation). Every one of the T*k rows of y is written exactly
+ * once; pad rows of act are never used for a real row.
+ *
+ *   act  [cap, I] bf16, device (from moe_grouped_gemm_gate_up_silu).
+ *   w2   [E, H, I] bf16, device.
+ *   y    [T*k, H] bf16, device, output, in (token, slot) order.
+ */
+int moe_grouped_gemm_down(const void* act, const void* w2, const int32_t* sorted_ids, const int32_t* block_expert,
+                          const int32_t* num_padded, int64_t T, int32_t k, int32_t H, int32_t I, int32_t E,
+                          int32_t block_m, int64_t cap, void* y, void* stream);
+
+/*
+ * Weighted sum of the k expert outputs of each token ([MoE]: expert outputs
+ * weighted by their scores and summed):
+ *   out[t, h] = sum_j topk_weights[t, j] * y[t*k + j, h]   (fp32 accumulation)
+ *
+ *   y             [T*k, H] bf16, device.
+ *   topk_weights  [T, k] fp32, device.
+ *   out           [T, H], device: bf16 (round to nearest even) when
+ *                 out_dtype == MOE_OUT_BF16, fp32 when MOE_OUT_FP32.
+ */
+int moe_combine(const void* y, const float* topk_weights, int64_t T, int32_t k, int32_t H, void* out,
+                int32_t out_dtype, void* stream);
+
+/* The block_m the library's GEMMs run fastest with for this routing shape
+ * (a tile-size choice only; every valid block_m gives the same result up to
+ * fp32 rounding of the accumulation order, which does not depend on
+ * block_m). Returns -1 on invalid arguments. */
+int32_t moe_pick_block_m(int64_t T, int32_t k, int32_t E);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

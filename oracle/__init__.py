@@ -14,8 +14,9 @@ function follows the passage cited in the C source:
   optional norm_topk_prob renormalisation.
 * ``align``           -- tokens grouped by expert (fused-backend paragraph),
   each group padded to block_m with the sentinel T*k.
-* ``expert_mlp``      -- one expert's gated MLP (GatedMLP on the "Models and
-  weight loading" page).
+* ``expert_gate_up``, ``expert_down``, ``expert_mlp`` -- one expert's gated
+  MLP and its two halves (GatedMLP on the "Models and weight loading" page).
+* ``combine``         -- the weighted sum of a token's k expert outputs.
 * ``moe_layer``       -- the whole layer, one token at a time.
 
 All of these are pinned by the tests in ``tests/test_oracle_*.py`` (brute
@@ -51,10 +52,22 @@ class OracleLib:
         lib.oracle_align.restype = i64
         lib.oracle_expert_mlp.argtypes = [p, p, p, i64, i64, p, p]
         lib.oracle_expert_mlp.restype = None
+        lib.oracle_expert_gate_up.argtypes = [p, p, i64, i64, p]
+        lib.oracle_expert_gate_up.restype = None
+        lib.oracle_expert_down.argtypes = [p, p, i64, i64, p]
+        lib.oracle_expert_down.restype = None
+        lib.oracle_combine.argtypes = [p, p, i64, i64, p]
+        lib.oracle_combine.restype = None
         lib.oracle_moe_layer.argtypes = [p, p, p, p, p, i64, i64, i64, i64, i64, ci, p, i64, p, p, p]
         lib.oracle_moe_layer.restype = None
+        lib.oracle_max_threads.argtypes = []
+        lib.oracle_max_threads.restype = ci
         self.path = path
         self._lib = lib
+
+    def max_threads(self) -> int:
+        """OpenMP threads the oracle's parallel loops use."""
+        return int(self._lib.oracle_max_threads())
 
     def router_logits(self, x: np.ndarray, w_router: np.ndarray, bias: Optional[np.ndarray] = None) -> np.ndarray:
         """fp64 logits [T, E] from bf16 x [T, H] and w_router [E, H] (+ fp32 bias [E])."""
@@ -110,6 +123,40 @@ class OracleLib:
         for r in range(x.shape[0]):
             self._lib.oracle_expert_mlp(x[r].ctypes.data, w13_e.ctypes.data, w2_e.ctypes.data, H, I,
                                         act.ctypes.data, out[r].ctypes.data)
+        return out
+
+    def expert_gate_up(self, x: np.ndarray, w13_e: np.ndarray) -> np.ndarray:
+        """silu(gate) * up of one expert for fp64 rows x [n, H]; w13_e [2I, H] bf16 -> [n, I]."""
+        x = np.ascontiguousarray(np.atleast_2d(x), dtype=np.float64)
+        w13_e = _u16(w13_e)
+        H = x.shape[1]
+        I = w13_e.shape[0] // 2
+        assert w13_e.shape == (2 * I, H)
+        out = np.empty((x.shape[0], I), dtype=np.float64)
+        for r in range(x.shape[0]):
+            self._lib.oracle_expert_gate_up(x[r].ctypes.data, w13_e.ctypes.data, H, I, out[r].ctypes.data)
+        return out
+
+    def expert_down(self, act: np.ndarray, w2_e: np.ndarray) -> np.ndarray:
+        """Down projection of one expert for fp64 rows act [n, I]; w2_e [H, I] bf16 -> [n, H]."""
+        act = np.ascontiguousarray(np.atleast_2d(act), dtype=np.float64)
+        w2_e = _u16(w2_e)
+        H, I = w2_e.shape
+        assert act.shape[1] == I
+        out = np.empty((act.shape[0], H), dtype=np.float64)
+        for r in range(act.shape[0]):
+            self._lib.oracle_expert_down(act[r].ctypes.data, w2_e.ctypes.data, H, I, out[r].ctypes.data)
+        return out
+
+    def combine(self, y: np.ndarray, w: np.ndarray) -> np.ndarray:
+        """out [T, H] = sum_j w[t, j] * y[t, j, :] for y [T, k, H], w [T, k] (fp64)."""
+        y = np.ascontiguousarray(y, dtype=np.float64)
+        w = np.ascontiguousarray(w, dtype=np.float64)
+        T, k, H = y.shape
+        assert w.shape == (T, k)
+        out = np.empty((T, H), dtype=np.float64)
+        for t in range(T):
+            self._lib.oracle_combine(y[t].ctypes.data, w[t].ctypes.data, k, H, out[t].ctypes.data)
         return out
 
     def moe_layer(self, x, w_router, w13, w2, k: int, norm_topk_prob: bool = True, bias=None,
@@ -196,6 +243,18 @@ def align(*a, **kw):
 
 def expert_mlp(*a, **kw):
     return default().expert_mlp(*a, **kw)
+
+
+def expert_gate_up(*a, **kw):
+    return default().expert_gate_up(*a, **kw)
+
+
+def expert_down(*a, **kw):
+    return default().expert_down(*a, **kw)
+
+
+def combine(*a, **kw):
+    return default().combine(*a, **kw)
 
 
 def moe_layer(*a, **kw):

@@ -37,9 +37,21 @@
  * bf16 inputs arrive as raw bit patterns and are widened exactly to float64.
  */
 #include <math.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+
+/* Threads an OpenMP parallel region of this library will use. */
+int oracle_max_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
 
 static double bf16_value(uint16_t bits) {
     uint32_t u = (uint32_t)bits << 16;
@@ -146,14 +158,12 @@ int64_t oracle_align(const int32_t* ids, int64_t T, int64_t k, int64_t E, int64_
     return off;
 }
 
-/* One expert's gated MLP [Models], section "Model structure":
+/* First half of one expert's gated MLP [Models], section "Model structure"
+ * (gate_up_proj, then silu(gate) * up):
  * g_i = sum_h x_h * w13[i, h], u_i = sum_h x_h * w13[I + i, h],
- * a_i = silu(g_i) * u_i with silu(z) = z / (1 + exp(-z)),
- * y_h = sum_i a_i * w2[h, i].
- * x: [H] float64, w13: [2I, H] bf16, w2: [H, I] bf16, act: [I] scratch,
- * y: [H]. */
-void oracle_expert_mlp(const double* x, const uint16_t* w13, const uint16_t* w2, int64_t H, int64_t I,
-                       double* act, double* y) {
+ * act_i = silu(g_i) * u_i with silu(z) = z / (1 + exp(-z)).
+ * x: [H] float64, w13: [2I, H] bf16, act: [I]. */
+void oracle_expert_gate_up(const double* x, const uint16_t* w13, int64_t H, int64_t I, double* act) {
     for (int64_t i = 0; i < I; ++i) {
         double g = 0.0, u = 0.0;
         for (int64_t h = 0; h < H; ++h) {
@@ -162,11 +172,31 @@ void oracle_expert_mlp(const double* x, const uint16_t* w13, const uint16_t* w2,
         }
         act[i] = g / (1.0 + exp(-g)) * u;
     }
+}
+
+/* Second half [Models], "Model structure" (down_proj):
+ * y_h = sum_i act_i * w2[h, i]. act: [I] float64, w2: [H, I] bf16, y: [H]. */
+void oracle_expert_down(const double* act, const uint16_t* w2, int64_t H, int64_t I, double* y) {
     for (int64_t h = 0; h < H; ++h) {
         double s = 0.0;
         for (int64_t i = 0; i < I; ++i) s += act[i] * bf16_value(w2[h * I + i]);
         y[h] = s;
     }
+}
+
+/* One expert's whole gated MLP: gate_up then down. act: [I] scratch. */
+void oracle_expert_mlp(const double* x, const uint16_t* w13, const uint16_t* w2, int64_t H, int64_t I,
+                       double* act, double* y) {
+    oracle_expert_gate_up(x, w13, H, I, act);
+    oracle_expert_down(act, w2, H, I, y);
+}
+
+/* Weighted sum of one token's k expert outputs [MoE] ("weighted by softmax
+ * scores and summed"): out_h = sum_j w_j * y[j, h]. y: [k, H], w: [k]. */
+void oracle_combine(const double* y, const double* w, int64_t k, int64_t H, double* out) {
+    for (int64_t h = 0; h < H; ++h) out[h] = 0.0;
+    for (int64_t j = 0; j < k; ++j)
+        for (int64_t h = 0; h < H; ++h) out[h] += w[j] * y[j * H + h];
 }
 
 /* The whole layer for the listed tokens, one token at a time [MoE]:
@@ -186,7 +216,7 @@ void oracle_moe_layer(const uint16_t* x, const uint16_t* wr, const float* bias, 
         double* xr = (double*)malloc(sizeof(double) * (size_t)H);
         double* logits = (double*)malloc(sizeof(double) * (size_t)E);
         double* act = (double*)malloc(sizeof(double) * (size_t)I);
-        double* y = (double*)malloc(sizeof(double) * (size_t)H);
+        double* y = (double*)malloc(sizeof(double) * (size_t)(k * H));
         int32_t* ids = (int32_t*)malloc(sizeof(int32_t) * (size_t)k);
         double* w = (double*)malloc(sizeof(double) * (size_t)k);
 #pragma omp for schedule(dynamic, 1)
@@ -195,13 +225,11 @@ void oracle_moe_layer(const uint16_t* x, const uint16_t* wr, const float* bias, 
             for (int64_t h = 0; h < H; ++h) xr[h] = bf16_value(x[t * H + h]);
             oracle_router_logits(x + t * H, wr, bias, 1, H, E, logits);
             oracle_select_topk(logits, 1, E, k, norm_topk_prob, ids, w);
-            double* o = out + n * H;
-            for (int64_t h = 0; h < H; ++h) o[h] = 0.0;
             for (int64_t j = 0; j < k; ++j) {
                 int64_t e = ids[j];
-                oracle_expert_mlp(xr, w13 + e * 2 * I * H, w2 + e * H * I, H, I, act, y);
-                for (int64_t h = 0; h < H; ++h) o[h] += w[j] * y[h];
+                oracle_expert_mlp(xr, w13 + e * 2 * I * H, w2 + e * H * I, H, I, act, y + j * H);
             }
+            oracle_combine(y, w, k, H, out + n * H);
             if (ids_out)
                 for (int64_t j = 0; j < k; ++j) ids_out[n * k + j] = ids[j];
             if (w_out)

@@ -1,0 +1,30 @@
+"""Fused sparse Mixture-of-Experts layer for AMD Instinct MI355X (gfx950).
+
+Router linear -> softmax -> top-k (optional renormalisation) -> tokens grouped
+by expert -> grouped gate/up GEMM with SiLU-and-mul -> grouped down GEMM ->
+weighted combine, each a hand-written HIP kernel in libmoe_mi355x.so (C ABI:
+include/moe_mi355x.h). This package is the thin Python binding over it.
+"""
+from ._lib import (  # noqa: F401
+    EXPORTS,
+    LIB_PATH,
+    MOE_ERR_HIP,
+    MOE_ERR_INVALID,
+    MOE_ERR_UNSUPPORTED,
+    MOE_ERR_WORKSPACE,
+    MOE_OK,
+    LibraryMissing,
+    MoEError,
+    lib,
+    moe_abi_version,
+    moe_align_by_expert,
+    moe_align_capacity,
+    moe_align_workspace_bytes,
+    moe_combine,
+    moe_grouped_gemm_down,
+    moe_grouped_gemm_gate_up_silu,
+    moe_last_error,
+    moe_pick_block_m,
+    moe_route,
+)
+from .layer import MoEBuffers, MoEConfig, allocate, moe_layer  # noqa: F401

@@ -1,0 +1,185 @@
+"""ctypes binding of libmoe_mi355x.so (the C ABI in include/moe_mi355x.h).
+
+Argument marshalling only: every step of the layer runs in the library's HIP
+kernels. The functions keep the C names; device buffers are torch tensors
+(checked for device, dtype and contiguity here), sizes are Python ints, and
+``stream`` defaults to torch's current stream on the tensors' device. A
+nonzero status raises ``MoEError`` with the library's message. There is no
+fallback: if the library is missing or does not load, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmoe_mi355x.so")
+
+MOE_OK = 0
+MOE_ERR_INVALID = -1
+MOE_ERR_UNSUPPORTED = -2
+MOE_ERR_HIP = -3
+MOE_ERR_WORKSPACE = -4
+MOE_OUT_BF16 = 0
+MOE_OUT_FP32 = 1
+
+EXPORTS = (
+    "moe_abi_version",
+    "moe_last_error",
+    "moe_route",
+    "moe_align_capacity",
+    "moe_align_workspace_bytes",
+    "moe_align_by_expert",
+    "moe_grouped_gemm_gate_up_silu",
+    "moe_grouped_gemm_down",
+    "moe_combine",
+    "moe_pick_block_m",
+)
+
+
+class MoEError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__(f"[{code}] {message}")
+        self.code = code
+
+
+class LibraryMissing(RuntimeError):
+    pass
+
+
+_lib = None
+
+
+def lib():
+    """The loaded library (raises LibraryMissing if it is not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise LibraryMissing(f"{LIB_PATH} is not built; run python -m sparse_mixture_experts_softmax_amd.build")
+        L = ctypes.CDLL(LIB_PATH)
+        p, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+        L.moe_abi_version.argtypes, L.moe_abi_version.restype = [], ctypes.c_int
+        L.moe_last_error.argtypes, L.moe_last_error.restype = [], ctypes.c_char_p
+        L.moe_route.argtypes = [p, p, p, p, p, p, i64, i32, i32, i32, i32, p]
+        L.moe_align_capacity.argtypes, L.moe_align_capacity.restype = [i64, i32, i32, i32], i64
+        L.moe_align_workspace_bytes.argtypes, L.moe_align_workspace_bytes.restype = [i64, i32, i32, i32], sz
+        L.moe_align_by_expert.argtypes = [p, i64, i32, i32, i32, p, p, p, p, p, sz, p]
+        L.moe_grouped_gemm_gate_up_silu.argtypes = [p, p, p, p, p, i64, i32, i32, i32, i32, i32, i64, p, p]
+        L.moe_grouped_gemm_down.argtypes = [p, p, p, p, p, i64, i32, i32, i32, i32, i32, i64, p, p]
+        L.moe_combine.argtypes = [p, p, i64, i32, i32, p, i32, p]
+        L.moe_pick_block_m.argtypes, L.moe_pick_block_m.restype = [i64, i32, i32], i32
+        for name in ("moe_route", "moe_align_by_expert", "moe_grouped_gemm_gate_up_silu", "moe_grouped_gemm_down",
+                     "moe_combine"):
+            getattr(L, name).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _check(rc: int):
+    if rc != MOE_OK:
+        raise MoEError(rc, lib().moe_last_error().decode())
+
+
+def _dev(t: Optional[torch.Tensor], dtype, name: str, optional: bool = False):
+    """data pointer of a contiguous GPU tensor of the given dtype (or None)."""
+    if t is None:
+        if optional:
+            return None
+        raise ValueError(f"{name} is required")
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr() if t.numel() else None
+
+
+def _stream(stream, *tensors) -> Optional[int]:
+    if stream is not None:
+        return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+    for t in tensors:
+        if isinstance(t, torch.Tensor) and t.is_cuda:
+            return torch.cuda.current_stream(t.device).cuda_stream
+    return torch.cuda.current_stream().cuda_stream
+
+
+def moe_abi_version() -> int:
+    return lib().moe_abi_version()
+
+
+def moe_last_error() -> str:
+    return lib().moe_last_error().decode()
+
+
+def moe_route(x, w_router, router_bias, logits, topk_ids, topk_weights, T: int, H: int, E: int, k: int,
+              norm_topk_prob: bool, stream=None):
+    """Router linear + softmax + top-k (+ renorm). ``x=None``: logits are an input."""
+    bf, f32, i32 = torch.bfloat16, torch.float32, torch.int32
+    args = (
+        _dev(x, bf, "x", optional=True),
+        _dev(w_router, bf, "w_router", optional=x is None),
+        _dev(router_bias, f32, "router_bias", optional=True),
+        _dev(logits, f32, "logits"),
+        _dev(topk_ids, i32, "topk_ids"),
+        _dev(topk_weights, f32, "topk_weights"),
+    )
+    _check(lib().moe_route(*args, T, H, E, k, int(bool(norm_topk_prob)), _stream(stream, logits)))
+
+
+def moe_align_capacity(T: int, k: int, E: int, block_m: int) -> int:
+    return lib().moe_align_capacity(T, k, E, block_m)
+
+
+def moe_align_workspace_bytes(T: int, k: int, E: int, block_m: int) -> int:
+    return lib().moe_align_workspace_bytes(T, k, E, block_m)
+
+
+def moe_pick_block_m(T: int, k: int, E: int) -> int:
+    return lib().moe_pick_block_m(T, k, E)
+
+
+def moe_align_by_expert(topk_ids, T: int, k: int, E: int, block_m: int, sorted_ids, block_expert, expert_counts,
+                        num_padded, workspace=None, stream=None):
+    i32 = torch.int32
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        if not workspace.is_cuda or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous GPU tensor")
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    _check(lib().moe_align_by_expert(_dev(topk_ids, i32, "topk_ids"), T, k, E, block_m,
+                                     _dev(sorted_ids, i32, "sorted_ids"), _dev(block_expert, i32, "block_expert"),
+                                     _dev(expert_counts, i32, "expert_counts"), _dev(num_padded, i32, "num_padded"),
+                                     ws_ptr, ws_bytes, _stream(stream, topk_ids)))
+
+
+def moe_grouped_gemm_gate_up_silu(x, w13, sorted_ids, block_expert, num_padded, T: int, k: int, H: int, I: int,
+                                  E: int, block_m: int, cap: int, act, stream=None):
+    bf, i32 = torch.bfloat16, torch.int32
+    _check(lib().moe_grouped_gemm_gate_up_silu(_dev(x, bf, "x"), _dev(w13, bf, "w13"),
+                                               _dev(sorted_ids, i32, "sorted_ids"),
+                                               _dev(block_expert, i32, "block_expert"),
+                                               _dev(num_padded, i32, "num_padded"), T, k, H, I, E, block_m, cap,
+                                               _dev(act, bf, "act"), _stream(stream, x)))
+
+
+def moe_grouped_gemm_down(act, w2, sorted_ids, block_expert, num_padded, T: int, k: int, H: int, I: int, E: int,
+                          block_m: int, cap: int, y, stream=None):
+    bf, i32 = torch.bfloat16, torch.int32
+    _check(lib().moe_grouped_gemm_down(_dev(act, bf, "act"), _dev(w2, bf, "w2"), _dev(sorted_ids, i32, "sorted_ids"),
+                                       _dev(block_expert, i32, "block_expert"), _dev(num_padded, i32, "num_padded"),
+                                       T, k, H, I, E, block_m, cap, _dev(y, bf, "y"), _stream(stream, act)))
+
+
+def moe_combine(y, topk_weights, T: int, k: int, H: int, out, stream=None):
+    """``out`` dtype (bf16 or fp32) selects the output precision."""
+    if out is None or out.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("out must be a bf16 or fp32 tensor")
+    od = MOE_OUT_FP32 if out.dtype == torch.float32 else MOE_OUT_BF16
+    _check(lib().moe_combine(_dev(y, torch.bfloat16, "y"), _dev(topk_weights, torch.float32, "topk_weights"), T, k, H,
+                             _dev(out, out.dtype, "out"), od, _stream(stream, y)))

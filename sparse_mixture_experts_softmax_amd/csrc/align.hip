@@ -1,0 +1,211 @@
+// moe_align_by_expert: group (token, slot) pairs by expert, each group
+// padded to the GEMM row tile, stable (ascending flat index inside a group)
+// and deterministic.
+//
+// The flat pairs are cut into tiles of kAlignTile entries. Kernel 1 counts
+// each tile's pairs per expert into the workspace (LDS atomics: the counts do
+// not depend on their order). Kernel 2 runs one workgroup per tile: it reads
+// every tile's counts, forms the expert totals, the padded exclusive scan and
+// the number of pairs of each expert in earlier tiles, then scatters its own
+// tile in rounds of 256 entries. Inside a round a pair's rank among the
+// earlier pairs of the same expert comes from wave ballots over the bits of
+// the expert id (the same-expert lane mask) plus per-wave counts in LDS, so
+// positions follow flat-index order exactly. Each workgroup also writes the
+// sentinel into the pad rows and the block owners of its share of the
+// capacity. When all pairs fit one tile, kernel 2 counts them itself and
+// kernel 1 is skipped.
+#include "abi_util.h"
+#include "moe_common.h"
+
+namespace moe {
+
+constexpr int kAlignTile = 4096;
+constexpr int kAlignThreads = 256;
+constexpr int kAlignWaves = kAlignThreads / kWave;
+
+__global__ __launch_bounds__(kAlignThreads) void align_hist_kernel(const int32_t* __restrict__ ids, int64_t n, int E,
+                                                                   int32_t* __restrict__ ws) {
+    __shared__ int cnt[kMaxExperts];
+    for (int e = threadIdx.x; e < E; e += blockDim.x) cnt[e] = 0;
+    __syncthreads();
+    const int64_t start = (int64_t)blockIdx.x * kAlignTile;
+    const int64_t end = min(n, start + kAlignTile);
+    for (int64_t i = start + threadIdx.x; i < end; i += blockDim.x) {
+        const int e = ids[i];
+        if ((unsigned)e < (unsigned)E) atomicAdd(&cnt[e], 1);
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += blockDim.x) ws[(int64_t)blockIdx.x * E + e] = cnt[e];
+}
+
+// Inclusive scan of v over the workgroup's first E threads' values (E <= 256),
+// Hillis-Steele in LDS. Returns the inclusive prefix for thread tid < E.
+__device__ int block_inclusive_scan(int v, int* buf, int E) {
+    const int tid = threadIdx.x;
+    if (tid < kMaxExperts) buf[tid] = tid < E ? v : 0;
+    __syncthreads();
+    for (int d = 1; d < kMaxExperts; d <<= 1) {
+        int add = 0;
+        if (tid < kMaxExperts && tid >= d) add = buf[tid - d];
+        __syncthreads();
+        if (tid < kMaxExperts) buf[tid] += add;
+        __syncthreads();
+    }
+    return tid < kMaxExperts ? buf[tid] : 0;
+}
+
+__global__ __launch_bounds__(kAlignThreads) void align_scatter_kernel(
+    const int32_t* __restrict__ ids, int64_t n, int E, int BM, int64_t cap, int ntiles,
+    const int32_t* __restrict__ ws, int fused_hist, int32_t* __restrict__ sorted_ids,
+    int32_t* __restrict__ block_expert, int32_t* __restrict__ counts_out, int32_t* __restrict__ num_padded) {
+    __shared__ int total[kMaxExperts];    // c_e
+    __shared__ int base[kMaxExperts];     // next position of this tile's pairs of expert e (relative to off)
+    __shared__ int off[kMaxExperts + 1];  // padded exclusive scan; off[E] = num_padded
+    __shared__ int scan_buf[kMaxExperts];
+    __shared__ int wcnt[kAlignWaves][kMaxExperts];
+    const int tid = threadIdx.x;
+    const int lane = tid % kWave, wave = tid / kWave;
+    const int tile = blockIdx.x;
+    const int64_t start = (int64_t)tile * kAlignTile;
+    const int64_t end = min(n, start + kAlignTile);
+
+    if (fused_hist) {
+        for (int e = tid; e < kMaxExperts; e += blockDim.x) total[e] = 0;
+        __syncthreads();
+        for (int64_t i = start + tid; i < end; i += blockDim.x) {
+            const int e = ids[i];
+            if ((unsigned)e < (unsigned)E) atomicAdd(&total[e], 1);
+        }
+        __syncthreads();
+        if (tid < E) base[tid] = 0;
+    } else if (tid < E) {
+        int tot = 0, pre = 0;
+        for (int t = 0; t < ntiles; ++t) {
+            const int h = ws[(int64_t)t * E + tid];
+            if (t < tile) pre += h;
+            tot += h;
+        }
+        total[tid] = tot;
+        base[tid] = pre;
+    }
+    for (int i = tid; i < kAlignWaves * kMaxExperts; i += blockDim.x) (&wcnt[0][0])[i] = 0;
+    __syncthreads();
+
+    const int padded = tid < E ? (total[tid] + BM - 1) / BM * BM : 0;
+    const int incl = block_inclusive_scan(padded, scan_buf, E);
+    if (tid < E) off[tid] = incl - padded;
+    if (tid == E - 1) off[E] = incl;
+    __syncthreads();
+    const int npad = off[E];
+    if (tile == 0) {
+        if (tid < E) counts_out[tid] = total[tid];
+        if (tid == 0) *num_padded = npad;
+    }
+
+    // Pad rows and block owners for this workgroup's share of [0, cap).
+    const int64_t nblocks = cap / BM;
+    const int64_t blocks_per = (nblocks + ntiles - 1) / ntiles;
+    const int64_t b_lo = (int64_t)tile * blocks_per, b_hi = min(nblocks, b_lo + blocks_per);
+    for (int64_t r = b_lo * BM + tid; r < b_hi * BM; r += blockDim.x) {
+        if (r >= npad) {
+            sorted_ids[r] = (int32_t)n;
+            if (r % BM == 0) block_expert[r / BM] = -1;
+            continue;
+        }
+        int lo = 0, hi = E - 1;  // largest e with off[e] <= r
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) / 2;
+            if (off[mid] <= r) lo = mid;
+            else hi = mid - 1;
+        }
+        if (r - off[lo] >= total[lo]) sorted_ids[r] = (int32_t)n;
+        if (r % BM == 0) block_expert[r / BM] = lo;
+    }
+
+    // Stable scatter of this tile's pairs.
+    const unsigned long long below = (1ull << lane) - 1ull;
+    for (int64_t r0 = start; r0 < end; r0 += blockDim.x) {
+        const int64_t i = r0 + tid;
+        int e = i < end ? ids[i] : -1;
+        if ((unsigned)e >= (unsigned)E) e = -1;
+        const bool valid = e >= 0;
+        unsigned long long same = __ballot(valid);
+#pragma unroll
+        for (int b = 0; b < 8; ++b) {
+            const unsigned long long m = __ballot(valid && ((e >> b) & 1));
+            same &= ((e >> b) & 1) ? m : ~m;
+        }
+        const int rank = __popcll(same & below);
+        if (valid && rank == 0) wcnt[wave][e] = __popcll(same);
+        __syncthreads();
+        if (valid) {
+            int pos = off[e] + base[e] + rank;
+            for (int w = 0; w < wave; ++w) pos += wcnt[w][e];
+            sorted_ids[pos] = (int32_t)i;
+        }
+        __syncthreads();
+        if (tid < E) {
+            int s = 0;
+#pragma unroll
+            for (int w = 0; w < kAlignWaves; ++w) {
+                s += wcnt[w][tid];
+                wcnt[w][tid] = 0;
+            }
+            base[tid] += s;
+        }
+        __syncthreads();
+    }
+}
+
+static int64_t align_ntiles(int64_t T, int32_t k) { return (T * k + kAlignTile - 1) / kAlignTile; }
+
+}  // namespace moe
+
+extern "C" int64_t moe_align_capacity(int64_t T, int32_t k, int32_t E, int32_t block_m) {
+    if (T < 0 || k < 1 || E < 1 || !moe::valid_block_m(block_m)) return -1;
+    const int64_t n = T * k;
+    const int64_t c = n + (n < E ? n : E) * (int64_t)(block_m - 1);
+    return (c + block_m - 1) / block_m * block_m;
+}
+
+extern "C" size_t moe_align_workspace_bytes(int64_t T, int32_t k, int32_t E, int32_t block_m) {
+    if (T < 0 || k < 1 || E < 1 || !moe::valid_block_m(block_m)) return 0;
+    const int64_t ntiles = moe::align_ntiles(T, k);
+    return ntiles <= 1 ? 0 : (size_t)ntiles * (size_t)E * sizeof(int32_t);
+}
+
+extern "C" int moe_align_by_expert(const int32_t* topk_ids, int64_t T, int32_t k, int32_t E, int32_t block_m,
+                                   int32_t* sorted_ids, int32_t* block_expert, int32_t* expert_counts,
+                                   int32_t* num_padded, void* workspace, size_t workspace_bytes, void* stream) {
+    using namespace moe;
+    clear_error();
+    if (T < 0 || k < 0 || E < 0) return set_error(MOE_ERR_INVALID, "moe_align_by_expert: negative size");
+    if (E < 1 || E > kMaxExperts)
+        return set_error(MOE_ERR_UNSUPPORTED, "moe_align_by_expert: E=%d outside [1, 256]", E);
+    if (k < 1 || k > E || k > kMaxTopK) return set_error(MOE_ERR_UNSUPPORTED, "moe_align_by_expert: k=%d invalid", k);
+    if (!valid_block_m(block_m))
+        return set_error(MOE_ERR_UNSUPPORTED, "moe_align_by_expert: block_m=%d not in {16,32,64,128}", block_m);
+    if (T * (int64_t)k >= ((int64_t)1 << 31))
+        return set_error(MOE_ERR_UNSUPPORTED, "moe_align_by_expert: T*k too large");
+    if (T == 0) return MOE_OK;
+    if (!topk_ids || !sorted_ids || !block_expert || !expert_counts || !num_padded)
+        return set_error(MOE_ERR_INVALID, "moe_align_by_expert: required pointer is NULL");
+    const int64_t ntiles = align_ntiles(T, k);
+    const size_t need = moe_align_workspace_bytes(T, k, E, block_m);
+    if (need > 0 && (workspace == nullptr || workspace_bytes < need))
+        return set_error(MOE_ERR_WORKSPACE, "moe_align_by_expert: workspace of %zu bytes needed, %zu given", need,
+                         workspace_bytes);
+    const int64_t cap = moe_align_capacity(T, k, E, block_m);
+    const int64_t n = T * k;
+    hipStream_t s = (hipStream_t)stream;
+    if (ntiles > 1) {
+        hipLaunchKernelGGL(align_hist_kernel, dim3((unsigned)ntiles), dim3(kAlignThreads), 0, s, topk_ids, n, (int)E,
+                           (int32_t*)workspace);
+        int rc = check_launch("moe_align_by_expert (histogram)");
+        if (rc) return rc;
+    }
+    hipLaunchKernelGGL(align_scatter_kernel, dim3((unsigned)ntiles), dim3(kAlignThreads), 0, s, topk_ids, n, (int)E,
+                       (int)block_m, cap, (int)ntiles, (const int32_t*)workspace, (int)(ntiles <= 1), sorted_ids,
+                       block_expert, expert_counts, num_padded);
+    return check_launch("moe_align_by_expert (scatter)");
+}

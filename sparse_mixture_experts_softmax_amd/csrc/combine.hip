@@ -1,0 +1,71 @@
+// moe_combine: out[t, :] = sum_j w[t, j] * y[t*k + j, :] in fp32.
+//
+// The k rows of a token are adjacent in y (token, slot order), so each
+// thread streams 16-byte chunks (8 bf16) of those rows and of the output
+// row: fully coalesced, HBM-bound. One workgroup per token, 256 threads; a
+// thread covers hidden positions 8*tid + 2048*m.
+#include "abi_util.h"
+#include "moe_common.h"
+
+namespace moe {
+
+constexpr int kCombineThreads = 256;
+
+template <bool OUT_F32>
+__global__ __launch_bounds__(kCombineThreads) void combine_kernel(const uint16_t* __restrict__ y,
+                                                                  const float* __restrict__ w, int k, int H,
+                                                                  void* __restrict__ out) {
+    const int64_t t = blockIdx.x;
+    const uint16_t* yt = y + t * k * (int64_t)H;
+    const float* wt = w + t * k;
+    for (int h = threadIdx.x * 8; h < H; h += kCombineThreads * 8) {
+        float acc[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) acc[q] = 0.f;
+        for (int j = 0; j < k; ++j) {
+            const float wj = wt[j];
+            const u32x4 v = *(const u32x4*)(yt + (int64_t)j * H + h);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                acc[2 * q] += wj * __uint_as_float(v[q] << 16);
+                acc[2 * q + 1] += wj * __uint_as_float(v[q] & 0xffff0000u);
+            }
+        }
+        if (OUT_F32) {
+            float* o = (float*)out + t * H + h;
+            *(f32x4*)o = f32x4{acc[0], acc[1], acc[2], acc[3]};
+            *(f32x4*)(o + 4) = f32x4{acc[4], acc[5], acc[6], acc[7]};
+        } else {
+            u32x4 p;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) p[q] = pack_bf16x2(acc[2 * q], acc[2 * q + 1]);
+            *(u32x4*)((uint16_t*)out + t * H + h) = p;
+        }
+    }
+}
+
+}  // namespace moe
+
+extern "C" int moe_combine(const void* y, const float* topk_weights, int64_t T, int32_t k, int32_t H, void* out,
+                           int32_t out_dtype, void* stream) {
+    using namespace moe;
+    clear_error();
+    if (T < 0 || k < 0 || H < 0) return set_error(MOE_ERR_INVALID, "moe_combine: negative size");
+    if (k < 1 || k > kMaxTopK) return set_error(MOE_ERR_UNSUPPORTED, "moe_combine: k=%d outside [1, 32]", k);
+    if (H == 0 || H % 64) return set_error(MOE_ERR_UNSUPPORTED, "moe_combine: H=%d is not a positive multiple of 64", H);
+    if (out_dtype != MOE_OUT_BF16 && out_dtype != MOE_OUT_FP32)
+        return set_error(MOE_ERR_INVALID, "moe_combine: out_dtype=%d is neither bf16 (0) nor fp32 (1)", out_dtype);
+    if (T * (int64_t)k >= ((int64_t)1 << 31)) return set_error(MOE_ERR_UNSUPPORTED, "moe_combine: T*k too large");
+    if (T == 0) return MOE_OK;
+    if (!y || !topk_weights || !out) return set_error(MOE_ERR_INVALID, "moe_combine: required pointer is NULL");
+    if (((uintptr_t)y | (uintptr_t)out) & 15)
+        return set_error(MOE_ERR_INVALID, "moe_combine: y and out must be 16-byte aligned");
+    if (T >= ((int64_t)1 << 31)) return set_error(MOE_ERR_UNSUPPORTED, "moe_combine: T too large");
+    if (out_dtype == MOE_OUT_FP32)
+        hipLaunchKernelGGL(combine_kernel<true>, dim3((unsigned)T), dim3(kCombineThreads), 0, (hipStream_t)stream,
+                           (const uint16_t*)y, topk_weights, (int)k, (int)H, out);
+    else
+        hipLaunchKernelGGL(combine_kernel<false>, dim3((unsigned)T), dim3(kCombineThreads), 0, (hipStream_t)stream,
+                           (const uint16_t*)y, topk_weights, (int)k, (int)H, out);
+    return check_launch("moe_combine");
+}

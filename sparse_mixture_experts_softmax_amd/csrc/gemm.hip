@@ -1,0 +1,310 @@
+// Grouped expert GEMMs on the matrix cores (v_mfma_f32_16x16x32_bf16, fp32
+// accumulation), one launch for all experts.
+//
+//   gate/up:  act[r, c] = silu(x[t] . w13[e, c]) * (x[t] . w13[e, I + c])
+//   down:     y[i, h]   = act[r] . w2[e, h]
+//
+// with r a row of the expert-grouped permutation, i = sorted_ids[r] the flat
+// (token, slot) index, t = i / k its token and e = block_expert[r / BM] the
+// expert owning the row block. Both operands are K-contiguous (x rows / act
+// rows and weight rows), so A and B fragments load the same way.
+//
+// Grid: one workgroup per (row block, N tile), row-block major; blocks past
+// num_padded (read on the device) return at once, so no host sync is needed.
+// Each workgroup stages BMxBK activation rows (gathered through sorted_ids
+// for gate/up) and BNxBK weight rows in LDS with 16-byte coalesced loads,
+// double-buffered: the next K tile is loaded into registers while the
+// current one feeds the MFMAs. For gate/up an N tile holds BN/2 gate rows and
+// the BN/2 matching up rows, so each wave owns the gate and up accumulators
+// of the same output columns and applies silu(g) * u in registers.
+#include "abi_util.h"
+#include "moe_common.h"
+
+namespace moe {
+
+template <int BM_, int BN_, bool GATED_>
+struct GemmCfg {
+    static constexpr int BM = BM_;
+    static constexpr int BN = BN_;
+    static constexpr bool GATED = GATED_;
+    static constexpr int BK = 64;
+    static constexpr int THREADS = 256;
+    static constexpr int WAVES = THREADS / kWave;
+    static constexpr int WAVES_M = BM >= 32 ? 2 : 1;
+    static constexpr int WAVES_N = WAVES / WAVES_M;
+    static constexpr int WTM = BM / WAVES_M;
+    static constexpr int WTN = BN / WAVES_N;
+    static constexpr int MT = WTM / 16;
+    static constexpr int NT = WTN / 16;
+    static constexpr int STRIDE = BK + 8;  // LDS row stride in elements (16-byte pad)
+    static constexpr int A_CHUNKS = BM * BK / 8;
+    static constexpr int B_CHUNKS = BN * BK / 8;
+    static constexpr int A_PER_T = (A_CHUNKS + THREADS - 1) / THREADS;
+    static constexpr int B_PER_T = (B_CHUNKS + THREADS - 1) / THREADS;
+    static_assert(MT >= 1 && NT >= 1, "tile too small");
+    static_assert(!GATED || NT % 2 == 0, "gated tile needs gate and up halves");
+};
+
+template <class C>
+__global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(
+    const uint16_t* __restrict__ a_src, const uint16_t* __restrict__ w, const int32_t* __restrict__ sorted_ids,
+    const int32_t* __restrict__ block_expert, const int32_t* __restrict__ num_padded, int k, int64_t n_pairs,
+    int K, int N_out, int n_tiles, uint16_t* __restrict__ out) {
+    constexpr int BM = C::BM, BN = C::BN, BK = C::BK, STRIDE = C::STRIDE;
+    __shared__ __attribute__((aligned(16))) uint16_t sA[2][BM * STRIDE];
+    __shared__ __attribute__((aligned(16))) uint16_t sB[2][BN * STRIDE];
+    __shared__ int64_t row_src[BM];  // gate/up: x row offset (-1 = zero row); down: y row (-1 = skip)
+
+    const int tid = threadIdx.x;
+    const int lane = tid % kWave, wave = tid / kWave;
+    const int mb = blockIdx.x / n_tiles;
+    const int tn = blockIdx.x % n_tiles;
+    if ((int64_t)mb * BM >= (int64_t)*num_padded) return;
+    const int e = block_expert[mb];
+    if (e < 0) return;
+
+    // weights: gate/up W13[e] is [2*N_out, K]; down W2[e] is [N_out, K]
+    const int64_t w_rows = C::GATED ? 2 * (int64_t)N_out : (int64_t)N_out;
+    const uint16_t* we = w + (int64_t)e * w_rows * K;
+
+    for (int i = tid; i < BM; i += C::THREADS) {
+        const int32_t id = sorted_ids[(int64_t)mb * BM + i];
+        const bool real = id >= 0 && (int64_t)id < n_pairs;
+        if (C::GATED) row_src[i] = real ? (int64_t)(id / k) * K : -1;
+        else row_src[i] = real ? (int64_t)id : -1;
+    }
+    __syncthreads();
+
+    // Global source of each thread's chunks (fixed across K tiles).
+    const uint16_t* a_ptr[C::A_PER_T];
+    bool a_ok[C::A_PER_T];
+#pragma unroll
+    for (int j = 0; j < C::A_PER_T; ++j) {
+        const int c = tid + j * C::THREADS;
+        const int row = c / (BK / 8), kc = (c % (BK / 8)) * 8;
+        a_ok[j] = c < C::A_CHUNKS;
+        if (C::GATED) {
+            const int64_t src = a_ok[j] ? row_src[row] : -1;
+            a_ok[j] = a_ok[j] && src >= 0;
+            a_ptr[j] = a_src + (src >= 0 ? src : 0) + kc;
+        } else {
+            a_ptr[j] = a_src + ((int64_t)mb * BM + row) * K + kc;
+        }
+    }
+    const uint16_t* b_ptr[C::B_PER_T];
+    bool b_ok[C::B_PER_T];
+#pragma unroll
+    for (int j = 0; j < C::B_PER_T; ++j) {
+        const int c = tid + j * C::THREADS;
+        const int row = c / (BK / 8), kc = (c % (BK / 8)) * 8;
+        int64_t wrow;
+        bool ok = c < C::B_CHUNKS;
+        if (C::GATED) {
+            const int half = BN / 2;
+            const int col = tn * half + (row % half);  // output column this weight row feeds
+            ok = ok && col < N_out;
+            wrow = (row < half) ? col : (int64_t)N_out + col;
+        } else {
+            const int col = tn * BN + row;
+            ok = ok && col < N_out;
+            wrow = col;
+        }
+        b_ok[j] = ok;
+        b_ptr[j] = we + (ok ? wrow : 0) * K + kc;
+    }
+
+    u32x4 ra[C::A_PER_T], rb[C::B_PER_T];
+    auto load_tile = [&](int kt) {
+        const int k0 = kt * BK;
+#pragma unroll
+        for (int j = 0; j < C::A_PER_T; ++j) {
+            const int kc = ((tid + j * C::THREADS) % (BK / 8)) * 8;
+            ra[j] = (a_ok[j] && k0 + kc < K) ? *(const u32x4*)(a_ptr[j] + k0) : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int j = 0; j < C::B_PER_T; ++j) {
+            const int kc = ((tid + j * C::THREADS) % (BK / 8)) * 8;
+            rb[j] = (b_ok[j] && k0 + kc < K) ? *(const u32x4*)(b_ptr[j] + k0) : u32x4{0u, 0u, 0u, 0u};
+        }
+    };
+    auto store_tile = [&](int buf) {
+#pragma unroll
+        for (int j = 0; j < C::A_PER_T; ++j) {
+            const int c = tid + j * C::THREADS;
+            if (c < C::A_CHUNKS) *(u32x4*)&sA[buf][(c / (BK / 8)) * STRIDE + (c % (BK / 8)) * 8] = ra[j];
+        }
+#pragma unroll
+        for (int j = 0; j < C::B_PER_T; ++j) {
+            const int c = tid + j * C::THREADS;
+            if (c < C::B_CHUNKS) *(u32x4*)&sB[buf][(c / (BK / 8)) * STRIDE + (c % (BK / 8)) * 8] = rb[j];
+        }
+    };
+
+    const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
+    f32x4 acc[C::MT][C::NT];
+#pragma unroll
+    for (int i = 0; i < C::MT; ++i)
+#pragma unroll
+        for (int j = 0; j < C::NT; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // LDS row of B that wave-tile column block j reads
+    auto b_lds_row = [&](int j) {
+        if (C::GATED) {
+            constexpr int HALF_NT = C::NT / 2;
+            const int g = j % HALF_NT;
+            return (j < HALF_NT ? 0 : BN / 2) + wn * (C::WTN / 2) + g * 16;
+        }
+        return wn * C::WTN + j * 16;
+    };
+
+    const int nk = (K + BK - 1) / BK;
+    load_tile(0);
+    store_tile(0);
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+        const int buf = kt & 1;
+        if (kt + 1 < nk) load_tile(kt + 1);
+#pragma unroll
+        for (int ks = 0; ks < BK / 32; ++ks) {
+            const int kof = ks * 32 + (lane / 16) * 8;
+            u32x4 fa[C::MT], fb[C::NT];
+#pragma unroll
+            for (int i = 0; i < C::MT; ++i)
+                fa[i] = *(const u32x4*)&sA[buf][(wm * C::WTM + i * 16 + lane % 16) * STRIDE + kof];
+#pragma unroll
+            for (int j = 0; j < C::NT; ++j) fb[j] = *(const u32x4*)&sB[buf][(b_lds_row(j) + lane % 16) * STRIDE + kof];
+#pragma unroll
+            for (int i = 0; i < C::MT; ++i)
+#pragma unroll
+                for (int j = 0; j < C::NT; ++j) acc[i][j] = mfma16x16x32(fa[i], fb[j], acc[i][j]);
+        }
+        if (kt + 1 < nk) store_tile(buf ^ 1);
+        __syncthreads();
+    }
+
+    // Epilogue. Lane holds rows 4*(lane/16)+q, column lane%16 of each 16x16 tile.
+    if (C::GATED) {
+        constexpr int HALF_NT = C::NT / 2;
+#pragma unroll
+        for (int i = 0; i < C::MT; ++i) {
+#pragma unroll
+            for (int g = 0; g < HALF_NT; ++g) {
+                const int col = tn * (BN / 2) + wn * (C::WTN / 2) + g * 16 + lane % 16;
+                if (col >= N_out) continue;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int row = wm * C::WTM + i * 16 + (lane / 16) * 4 + q;
+                    const float v = silu(acc[i][g][q]) * acc[i][g + HALF_NT][q];
+                    out[((int64_t)mb * BM + row) * N_out + col] = f32_to_bf16(v);
+                }
+            }
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < C::MT; ++i) {
+#pragma unroll
+            for (int j = 0; j < C::NT; ++j) {
+                const int col = tn * BN + wn * C::WTN + j * 16 + lane % 16;
+                if (col >= N_out) continue;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int row = wm * C::WTM + i * 16 + (lane / 16) * 4 + q;
+                    const int64_t dst = row_src[row];
+                    if (dst >= 0) out[dst * N_out + col] = f32_to_bf16(acc[i][j][q]);
+                }
+            }
+        }
+    }
+}
+
+template <class C>
+static int launch_gemm(const void* a, const void* w, const int32_t* sorted_ids, const int32_t* block_expert,
+                       const int32_t* num_padded, int k, int64_t n_pairs, int K, int N_out, int64_t cap, void* out,
+                       hipStream_t s, const char* what) {
+    const int n_cols = C::GATED ? C::BN / 2 : C::BN;
+    const int n_tiles = (N_out + n_cols - 1) / n_cols;
+    const int64_t m_blocks = cap / C::BM;
+    const int64_t grid = m_blocks * n_tiles;
+    if (grid >= ((int64_t)1 << 31)) return set_error(MOE_ERR_UNSUPPORTED, "%s: grid too large", what);
+    hipLaunchKernelGGL(grouped_gemm_kernel<C>, dim3((unsigned)grid), dim3(C::THREADS), 0, s, (const uint16_t*)a,
+                       (const uint16_t*)w, sorted_ids, block_expert, num_padded, k, n_pairs, K, N_out, n_tiles,
+                       (uint16_t*)out);
+    return check_launch(what);
+}
+
+template <bool GATED>
+static int dispatch_gemm(int32_t block_m, const void* a, const void* w, const int32_t* sorted_ids,
+                         const int32_t* block_expert, const int32_t* num_padded, int k, int64_t n_pairs, int K,
+                         int N_out, int64_t cap, void* out, hipStream_t s, const char* what) {
+    switch (block_m) {
+        case 16:
+            return launch_gemm<GemmCfg<16, 128, GATED>>(a, w, sorted_ids, block_expert, num_padded, k, n_pairs, K,
+                                                       N_out, cap, out, s, what);
+        case 32:
+            return launch_gemm<GemmCfg<32, 128, GATED>>(a, w, sorted_ids, block_expert, num_padded, k, n_pairs, K,
+                                                       N_out, cap, out, s, what);
+        case 64:
+            return launch_gemm<GemmCfg<64, 128, GATED>>(a, w, sorted_ids, block_expert, num_padded, k, n_pairs, K,
+                                                       N_out, cap, out, s, what);
+        case 128:
+            return launch_gemm<GemmCfg<128, 128, GATED>>(a, w, sorted_ids, block_expert, num_padded, k, n_pairs, K,
+                                                        N_out, cap, out, s, what);
+    }
+    return set_error(MOE_ERR_UNSUPPORTED, "%s: block_m=%d not in {16,32,64,128}", what, block_m);
+}
+
+static int check_gemm_args(const char* fn, const void* a, const void* w, const int32_t* sorted_ids,
+                           const int32_t* block_expert, const int32_t* num_padded, int64_t T, int32_t k, int32_t H,
+                           int32_t I, int32_t E, int32_t block_m, int64_t cap, const void* out) {
+    int rc = check_shape(fn, T, H, E, k, I);
+    if (rc) return rc;
+    if (!valid_block_m(block_m)) return set_error(MOE_ERR_UNSUPPORTED, "%s: block_m=%d not in {16,32,64,128}", fn, block_m);
+    if (T == 0) return MOE_OK;
+    if (!a || !w || !sorted_ids || !block_expert || !num_padded || !out)
+        return set_error(MOE_ERR_INVALID, "%s: required pointer is NULL", fn);
+    if (((uintptr_t)a | (uintptr_t)w | (uintptr_t)out) & 15)
+        return set_error(MOE_ERR_INVALID, "%s: activation, weight and output pointers must be 16-byte aligned", fn);
+    const int64_t need = moe_align_capacity(T, k, E, block_m);
+    if (cap < need)
+        return set_error(MOE_ERR_WORKSPACE, "%s: cap=%lld below moe_align_capacity=%lld", fn, (long long)cap,
+                         (long long)need);
+    if (cap % block_m) return set_error(MOE_ERR_INVALID, "%s: cap must be a multiple of block_m", fn);
+    return MOE_OK;
+}
+
+}  // namespace moe
+
+extern "C" int moe_grouped_gemm_gate_up_silu(const void* x, const void* w13, const int32_t* sorted_ids,
+                                             const int32_t* block_expert, const int32_t* num_padded, int64_t T,
+                                             int32_t k, int32_t H, int32_t I, int32_t E, int32_t block_m, int64_t cap,
+                                             void* act, void* stream) {
+    using namespace moe;
+    clear_error();
+    const char* fn = "moe_grouped_gemm_gate_up_silu";
+    int rc = check_gemm_args(fn, x, w13, sorted_ids, block_expert, num_padded, T, k, H, I, E, block_m, cap, act);
+    if (rc || T == 0) return rc;
+    return dispatch_gemm<true>(block_m, x, w13, sorted_ids, block_expert, num_padded, k, T * k, H, I, cap, act,
+                               (hipStream_t)stream, fn);
+}
+
+extern "C" int moe_grouped_gemm_down(const void* act, const void* w2, const int32_t* sorted_ids,
+                                     const int32_t* block_expert, const int32_t* num_padded, int64_t T, int32_t k,
+                                     int32_t H, int32_t I, int32_t E, int32_t block_m, int64_t cap, void* y,
+                                     void* stream) {
+    using namespace moe;
+    clear_error();
+    const char* fn = "moe_grouped_gemm_down";
+    int rc = check_gemm_args(fn, act, w2, sorted_ids, block_expert, num_padded, T, k, H, I, E, block_m, cap, y);
+    if (rc || T == 0) return rc;
+    return dispatch_gemm<false>(block_m, act, w2, sorted_ids, block_expert, num_padded, k, T * k, I, H, cap, y,
+                                (hipStream_t)stream, fn);
+}
+
+extern "C" int32_t moe_pick_block_m(int64_t T, int32_t k, int32_t E) {
+    if (T < 0 || k < 1 || E < 1) return -1;
+    const double rows_per_expert = (double)T * k / E;
+    if (rows_per_expert <= 24) return 16;
+    if (rows_per_expert <= 96) return 32;
+    if (rows_per_expert <= 384) return 64;
+    return 128;
+}

@@ -1,0 +1,105 @@
+"""The whole sparse MoE layer: allocates the intermediates with torch and
+calls the five library entry points in order on one stream.
+
+MoEConfig keeps the MoE field names of the model configuration on the
+"Models and weight loading" page (hidden_size, num_experts,
+num_experts_per_tok, moe_intermediate_size, norm_topk_prob, hidden_act);
+like that page's GatedMLP, only the silu activation is accepted.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional
+
+import torch
+
+from . import _lib
+
+
+@dataclasses.dataclass(frozen=True)
+class MoEConfig:
+    hidden_size: int
+    num_experts: int
+    num_experts_per_tok: int
+    moe_intermediate_size: int
+    norm_topk_prob: bool = False
+    hidden_act: str = "silu"
+
+    def __post_init__(self):
+        if self.hidden_act != "silu":
+            raise ValueError(f"Unsupported activation: {self.hidden_act}")
+
+
+@dataclasses.dataclass
+class MoEBuffers:
+    """Intermediates of one layer call (kept for inspection by tests)."""
+
+    logits: torch.Tensor
+    topk_ids: torch.Tensor
+    topk_weights: torch.Tensor
+    sorted_ids: torch.Tensor
+    block_expert: torch.Tensor
+    expert_counts: torch.Tensor
+    num_padded: torch.Tensor
+    workspace: Optional[torch.Tensor]
+    act: torch.Tensor
+    y: torch.Tensor
+    out: torch.Tensor
+    block_m: int
+    cap: int
+
+
+def allocate(T: int, H: int, E: int, k: int, I: int, device, block_m: Optional[int] = None,
+             out_dtype=torch.bfloat16) -> MoEBuffers:
+    if block_m is None:
+        block_m = _lib.moe_pick_block_m(T, k, E)
+    cap = _lib.moe_align_capacity(T, k, E, block_m)
+    if cap < 0:
+        raise ValueError("invalid (T, k, E, block_m)")
+    ws_bytes = _lib.moe_align_workspace_bytes(T, k, E, block_m)
+    i32 = dict(dtype=torch.int32, device=device)
+    return MoEBuffers(
+        logits=torch.empty((T, E), dtype=torch.float32, device=device),
+        topk_ids=torch.empty((T, k), **i32),
+        topk_weights=torch.empty((T, k), dtype=torch.float32, device=device),
+        sorted_ids=torch.empty((cap,), **i32),
+        block_expert=torch.empty((cap // block_m,), **i32),
+        expert_counts=torch.empty((E,), **i32),
+        num_padded=torch.empty((1,), **i32),
+        workspace=torch.empty((ws_bytes,), dtype=torch.uint8, device=device) if ws_bytes else None,
+        act=torch.empty((cap, I), dtype=torch.bfloat16, device=device),
+        y=torch.empty((T * k, H), dtype=torch.bfloat16, device=device),
+        out=torch.empty((T, H), dtype=out_dtype, device=device),
+        block_m=block_m,
+        cap=cap,
+    )
+
+
+def moe_layer(x: torch.Tensor, w_router: torch.Tensor, w13: torch.Tensor, w2: torch.Tensor, *, top_k: int,
+              norm_topk_prob: bool = True, router_bias: Optional[torch.Tensor] = None,
+              block_m: Optional[int] = None, out_dtype=torch.bfloat16, buffers: Optional[MoEBuffers] = None,
+              stream=None) -> torch.Tensor:
+    """out[T, H] = sparse MoE layer of x[T, H] (no residual).
+
+    x [T, H], w_router [E, H], w13 [E, 2I, H] (gate rows, then up rows),
+    w2 [E, H, I]: bf16 on the GPU; router_bias [E] fp32 or None."""
+    if x.dim() != 2 or w_router.dim() != 2 or w13.dim() != 3 or w2.dim() != 3:
+        raise ValueError("x [T,H], w_router [E,H], w13 [E,2I,H], w2 [E,H,I] expected")
+    T, H = x.shape
+    E = w_router.shape[0]
+    I = w2.shape[2]
+    if w_router.shape[1] != H or tuple(w13.shape) != (E, 2 * I, H) or tuple(w2.shape) != (E, H, I):
+        raise ValueError(f"shape mismatch: x {tuple(x.shape)}, w_router {tuple(w_router.shape)}, "
+                         f"w13 {tuple(w13.shape)}, w2 {tuple(w2.shape)}")
+    k = int(top_k)
+    b = buffers if buffers is not None else allocate(T, H, E, k, I, x.device, block_m, out_dtype)
+    s = _lib._stream(stream, x)
+    _lib.moe_route(x, w_router, router_bias, b.logits, b.topk_ids, b.topk_weights, T, H, E, k, norm_topk_prob, s)
+    _lib.moe_align_by_expert(b.topk_ids, T, k, E, b.block_m, b.sorted_ids, b.block_expert, b.expert_counts,
+                             b.num_padded, b.workspace, s)
+    _lib.moe_grouped_gemm_gate_up_silu(x, w13, b.sorted_ids, b.block_expert, b.num_padded, T, k, H, I, E, b.block_m,
+                                       b.cap, b.act, s)
+    _lib.moe_grouped_gemm_down(b.act, w2, b.sorted_ids, b.block_expert, b.num_padded, T, k, H, I, E, b.block_m, b.cap,
+                               b.y, s)
+    _lib.moe_combine(b.y, b.topk_weights, T, k, H, b.out, s)
+    return b.out

@@ -1,0 +1,124 @@
+"""The C-ABI library on a machine without a GPU: it loads, exports every
+entry point the header declares, and rejects bad arguments on the host
+before enqueueing anything (no compute call is made here)."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import sparse_mixture_experts_softmax_amd as moe
+from sparse_mixture_experts_softmax_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_mi355x.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = moe.lib()
+    names = declared_functions()
+    assert len(names) >= 10, names
+    for name in names:
+        assert hasattr(L, name), f"{name} declared in the header but not exported"
+    assert set(names) == set(_lib.EXPORTS)
+    assert moe.moe_abi_version() == 1
+
+
+def test_capacity_and_workspace():
+    assert moe.moe_align_capacity(64, 8, 128, 16) == 512 + 128 * 15
+    assert moe.moe_align_capacity(16, 2, 8, 16) == 160  # 32 + 8*15 = 152 -> 160
+    assert moe.moe_align_capacity(1, 1, 256, 128) == 128
+    assert moe.moe_align_capacity(0, 8, 128, 64) == 0
+    assert moe.moe_align_capacity(10, 2, 8, 48) == -1
+    assert moe.moe_align_workspace_bytes(64, 8, 128, 16) == 0  # one tile: no workspace
+    assert moe.moe_align_workspace_bytes(16384, 8, 128, 64) == 32 * 128 * 4
+    for T, k, E in ((64, 8, 128), (4096, 8, 128), (16, 2, 8)):
+        assert moe.moe_pick_block_m(T, k, E) in (16, 32, 64, 128)
+
+
+def _raw():
+    return moe.lib()
+
+
+NULL = None
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every case below fails validation
+
+
+@pytest.mark.parametrize(
+    "args,code",
+    [
+        # moe_route(x, wr, bias, logits, ids, w, T, H, E, k, norm, stream)
+        ((FAKE, FAKE, NULL, FAKE, FAKE, FAKE, 4, 64, 300, 2, 1, NULL), _lib.MOE_ERR_UNSUPPORTED),
+        ((FAKE, FAKE, NULL, FAKE, FAKE, FAKE, 4, 64, 8, 9, 1, NULL), _lib.MOE_ERR_UNSUPPORTED),
+        ((FAKE, FAKE, NULL, FAKE, FAKE, FAKE, 4, 64, 64, 33, 1, NULL), _lib.MOE_ERR_UNSUPPORTED),
+        ((FAKE, FAKE, NULL, FAKE, FAKE, FAKE, 4, 96, 8, 2, 1, NULL), _lib.MOE_ERR_UNSUPPORTED),
+        ((FAKE, NULL, NULL, FAKE, FAKE, FAKE, 4, 64, 8, 2, 1, NULL), _lib.MOE_ERR_INVALID),
+        ((FAKE, FAKE, NULL, NULL, FAKE, FAKE, 4, 64, 8, 2, 1, NULL), _lib.MOE_ERR_INVALID),
+        ((FAKE, FAKE, NULL, FAKE, FAKE, FAKE, -1, 64, 8, 2, 1, NULL), _lib.MOE_ERR_INVALID),
+        ((FAKE, FAKE, NULL, FAKE, FAKE, FAKE, 0, 64, 8, 2, 1, NULL), _lib.MOE_OK),
+        ((NULL, NULL, NULL, FAKE, FAKE, FAKE, 0, 0, 8, 2, 1, NULL), _lib.MOE_OK),
+    ],
+)
+def test_route_validation(args, code):
+    assert _raw().moe_route(*args) == code
+    if code:
+        assert moe.moe_last_error().startswith("moe_route")
+
+
+def test_align_validation():
+    L = _raw()
+    # (ids, T, k, E, block_m, sorted, blk, counts, npad, ws, ws_bytes, stream)
+    assert L.moe_align_by_expert(FAKE, 16, 2, 8, 48, FAKE, FAKE, FAKE, FAKE, NULL, 0, NULL) == _lib.MOE_ERR_UNSUPPORTED
+    assert L.moe_align_by_expert(FAKE, 16, 9, 8, 16, FAKE, FAKE, FAKE, FAKE, NULL, 0, NULL) == _lib.MOE_ERR_UNSUPPORTED
+    assert L.moe_align_by_expert(NULL, 16, 2, 8, 16, FAKE, FAKE, FAKE, FAKE, NULL, 0, NULL) == _lib.MOE_ERR_INVALID
+    # several tiles need a workspace
+    assert L.moe_align_by_expert(FAKE, 4096, 8, 128, 64, FAKE, FAKE, FAKE, FAKE, NULL, 0, NULL) == _lib.MOE_ERR_WORKSPACE
+    assert L.moe_align_by_expert(FAKE, 4096, 8, 128, 64, FAKE, FAKE, FAKE, FAKE, FAKE, 100, NULL) == _lib.MOE_ERR_WORKSPACE
+    assert "workspace" in moe.moe_last_error()
+    assert L.moe_align_by_expert(NULL, 0, 2, 8, 16, NULL, NULL, NULL, NULL, NULL, 0, NULL) == _lib.MOE_OK
+
+
+def test_gemm_validation():
+    L = _raw()
+    for fn in (L.moe_grouped_gemm_gate_up_silu, L.moe_grouped_gemm_down):
+        # (a, w, sorted, blk, npad, T, k, H, I, E, block_m, cap, out, stream)
+        cap = moe.moe_align_capacity(16, 2, 8, 16)
+        assert fn(FAKE, FAKE, FAKE, FAKE, FAKE, 16, 2, 64, 48, 8, 16, cap, FAKE, NULL) == _lib.MOE_ERR_UNSUPPORTED
+        assert fn(FAKE, FAKE, FAKE, FAKE, FAKE, 16, 2, 100, 32, 8, 16, cap, FAKE, NULL) == _lib.MOE_ERR_UNSUPPORTED
+        assert fn(FAKE, FAKE, FAKE, FAKE, FAKE, 16, 2, 64, 32, 8, 24, cap, FAKE, NULL) == _lib.MOE_ERR_UNSUPPORTED
+        assert fn(FAKE, FAKE, FAKE, FAKE, FAKE, 16, 2, 64, 32, 8, 16, cap - 16, FAKE, NULL) == _lib.MOE_ERR_WORKSPACE
+        assert fn(FAKE, NULL, FAKE, FAKE, FAKE, 16, 2, 64, 32, 8, 16, cap, FAKE, NULL) == _lib.MOE_ERR_INVALID
+        misaligned = ctypes.c_void_p(0x1002)
+        assert fn(misaligned, FAKE, FAKE, FAKE, FAKE, 16, 2, 64, 32, 8, 16, cap, FAKE, NULL) == _lib.MOE_ERR_INVALID
+        assert fn(NULL, NULL, NULL, NULL, NULL, 0, 2, 64, 32, 8, 16, 0, NULL, NULL) == _lib.MOE_OK
+
+
+def test_combine_validation():
+    L = _raw()
+    assert L.moe_combine(FAKE, FAKE, 4, 2, 64, FAKE, 7, NULL) == _lib.MOE_ERR_INVALID
+    assert L.moe_combine(FAKE, FAKE, 4, 33, 64, FAKE, 0, NULL) == _lib.MOE_ERR_UNSUPPORTED
+    assert L.moe_combine(FAKE, FAKE, 4, 2, 32, FAKE, 0, NULL) == _lib.MOE_ERR_UNSUPPORTED
+    assert L.moe_combine(NULL, FAKE, 4, 2, 64, FAKE, 0, NULL) == _lib.MOE_ERR_INVALID
+    assert L.moe_combine(NULL, NULL, 0, 2, 64, NULL, 0, NULL) == _lib.MOE_OK
+
+
+def test_python_binding_rejects_host_tensors_and_wrong_dtypes():
+    x = torch.zeros(4, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU"):
+        moe.moe_combine(torch.zeros(8, 64, dtype=torch.bfloat16), torch.zeros(4, 2), 4, 2, 64, x)
+    with pytest.raises(TypeError):
+        moe.moe_combine(torch.zeros(8, 64), torch.zeros(4, 2), 4, 2, 64, x)
+    with pytest.raises(ValueError, match="Unsupported activation"):
+        moe.MoEConfig(64, 8, 2, 32, hidden_act="gelu")
+
+
+def test_status_raises_with_message():
+    with pytest.raises(moe.MoEError, match="E=300"):
+        _lib._check(_raw().moe_route(FAKE, FAKE, NULL, FAKE, FAKE, FAKE, 4, 64, 300, 2, 1, NULL))

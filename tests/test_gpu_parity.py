@@ -1,0 +1,319 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Routing ids and the expert-grouped permutation are compared bit for bit
+(given the same fp32 logits); each GEMM and the combine are compared with
+the oracle step they implement, fed the GPU's own upstream intermediate;
+the whole layer is compared with the oracle on all five workloads within
+max|err| <= 2e-2 * rms(out) + 1e-3 (and, on the tiny workload, also without
+the 1e-3 floor)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import sparse_mixture_experts_softmax_amd as moe
+from gpu_cases import (CONFIG_NAMES, bf16_tensor, custom_inputs, device_inputs, host_inputs, layer_tolerance, log,
+                       logits_bound, run_layer, sample_tokens, to_bits)
+
+pytestmark = pytest.mark.gpu
+
+NAN_BF16 = 0x7FC0
+
+
+def _f64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def elem_close(gpu, ref, rel=2.0 ** -8, floor_frac=1e-3, what=""):
+    """|gpu - ref| <= rel*|ref| + floor_frac*rms(ref) elementwise: bf16
+    rounding of the stored result (<= 2^-9 relative) plus fp32 accumulation
+    (orders of magnitude below the floor)."""
+    gpu, ref = np.asarray(gpu, np.float64), np.asarray(ref, np.float64)
+    rms = float(np.sqrt(np.mean(ref ** 2))) if ref.size else 0.0
+    bound = rel * np.abs(ref) + floor_frac * rms
+    err = np.abs(gpu - ref)
+    bad = err > bound
+    assert not bad.any(), f"{what}: {bad.sum()} of {bad.size} elements out of bound; max err {err.max():.3e}, rms {rms:.3e}"
+    return float(err.max()) if err.size else 0.0
+
+
+# ----------------------------------------------------------------------------
+# Routing
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("name", CONFIG_NAMES)
+def test_route_bitexact_given_logits(name):
+    log(f"route {name}")
+    inp = host_inputs(name)
+    s = inp.shape
+    dev = device_inputs(inp, key=name)
+    logits = torch.empty((s.T, s.E), dtype=torch.float32, device="cuda")
+    ids = torch.empty((s.T, s.k), dtype=torch.int32, device="cuda")
+    w = torch.empty((s.T, s.k), dtype=torch.float32, device="cuda")
+    moe.moe_route(dev["x"], dev["w_router"], dev["bias"], logits, ids, w, s.T, s.H, s.E, s.k, s.norm_topk_prob)
+    torch.cuda.synchronize()
+    lg = logits.cpu().numpy()
+    o_ids, o_w = oracle.select_topk(lg, s.k, s.norm_topk_prob)
+    assert np.array_equal(ids.cpu().numpy(), o_ids)
+    assert np.abs(w.cpu().numpy() - o_w).max() <= 1e-6
+    toks = sample_tokens(s.T, 256)
+    ref = oracle.router_logits(inp.x[toks], inp.w_router, inp.router_bias)
+    assert (np.abs(lg[toks] - ref) <= logits_bound(inp, toks)).all()
+
+
+@pytest.mark.parametrize("E,k,norm", [(8, 2, True), (128, 8, True), (128, 8, False), (256, 32, True), (5, 5, False),
+                                      (1, 1, True)])
+def test_route_ties_from_given_logits(E, k, norm):
+    """Integer-valued logits force ties: lower expert index first."""
+    rng = np.random.default_rng(E * 100 + k)
+    T = 203
+    lg = rng.integers(-3, 4, size=(T, E)).astype(np.float32)
+    logits = torch.from_numpy(lg).cuda()
+    ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    moe.moe_route(None, None, None, logits, ids, w, T, 0, E, k, norm)
+    torch.cuda.synchronize()
+    o_ids, o_w = oracle.select_topk(lg, k, norm)
+    assert np.array_equal(ids.cpu().numpy(), o_ids)
+    assert np.abs(w.cpu().numpy() - o_w).max() <= 1e-6
+    assert np.array_equal(logits.cpu().numpy(), lg)  # logits are input only
+
+
+# ----------------------------------------------------------------------------
+# Expert-grouped permutation
+# ----------------------------------------------------------------------------
+def _align_gpu(ids_np, E, bm):
+    T, k = ids_np.shape
+    cap = moe.moe_align_capacity(T, k, E, bm)
+    ids = torch.from_numpy(np.ascontiguousarray(ids_np, dtype=np.int32)).cuda()
+    sorted_ids = torch.full((cap,), -7, dtype=torch.int32, device="cuda")
+    block_expert = torch.full((cap // bm,), -7, dtype=torch.int32, device="cuda")
+    counts = torch.empty((E,), dtype=torch.int32, device="cuda")
+    npad = torch.empty((1,), dtype=torch.int32, device="cuda")
+    wsb = moe.moe_align_workspace_bytes(T, k, E, bm)
+    ws = torch.empty((wsb,), dtype=torch.uint8, device="cuda") if wsb else None
+    moe.moe_align_by_expert(ids, T, k, E, bm, sorted_ids, block_expert, counts, npad, ws)
+    torch.cuda.synchronize()
+    return sorted_ids.cpu().numpy(), block_expert.cpu().numpy(), counts.cpu().numpy(), int(npad.item())
+
+
+def _check_align(ids_np, E, bm):
+    g = _align_gpu(ids_np, E, bm)
+    o = oracle.align(ids_np, E, bm)
+    assert np.array_equal(g[0], o[0]), "sorted_ids"
+    assert np.array_equal(g[1], o[1]), "block_expert"
+    assert np.array_equal(g[2], o[2]), "expert_counts"
+    assert g[3] == o[3], "num_padded"
+
+
+@pytest.mark.parametrize("name", CONFIG_NAMES)
+@pytest.mark.parametrize("bm", [16, 32, 64, 128])
+def test_align_bitexact_on_routed_ids(name, bm):
+    inp = host_inputs(name)
+    s = inp.shape
+    ids, _ = oracle.select_topk(oracle.router_logits(inp.x, inp.w_router, inp.router_bias), s.k) if s.T <= 64 else (
+        None, None)
+    if ids is None:  # large workloads: route on the GPU (bit-exact by the routing test)
+        dev = device_inputs(inp, key=name)
+        logits = torch.empty((s.T, s.E), dtype=torch.float32, device="cuda")
+        idt = torch.empty((s.T, s.k), dtype=torch.int32, device="cuda")
+        w = torch.empty((s.T, s.k), dtype=torch.float32, device="cuda")
+        moe.moe_route(dev["x"], dev["w_router"], dev["bias"], logits, idt, w, s.T, s.H, s.E, s.k, True)
+        ids = idt.cpu().numpy()
+    _check_align(ids, s.E, bm)
+
+
+@pytest.mark.parametrize("T,k,E,bm", [(1, 1, 1, 16), (1, 8, 128, 128), (512, 8, 128, 16), (513, 8, 128, 64),
+                                      (4097, 1, 3, 32), (3000, 32, 256, 128), (777, 5, 7, 16), (20000, 2, 2, 64)])
+def test_align_bitexact_edge_shapes(T, k, E, bm):
+    rng = np.random.default_rng(T + k + E)
+    p = rng.dirichlet(np.full(E, 0.2))
+    ids = np.stack([rng.choice(E, size=k, replace=False, p=p) if np.count_nonzero(p) >= k
+                    else rng.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32)
+    _check_align(ids, E, bm)
+
+
+# ----------------------------------------------------------------------------
+# Each kernel against the oracle step it implements
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("name", ["tiny", "decode", "prefill", "large"])
+def test_gemms_and_combine_against_oracle_steps(name):
+    log(f"steps {name}")
+    inp = host_inputs(name)
+    s = inp.shape
+    dev = device_inputs(inp, key=name)
+    out, b = run_layer(inp, dev)
+    sorted_ids = b.sorted_ids.cpu().numpy()
+    block_expert = b.block_expert.cpu().numpy()
+    npad = int(b.num_padded.item())
+    n = s.T * s.k
+    rows = np.nonzero(sorted_ids[:npad] != n)[0]
+    pads = np.nonzero(sorted_ids[:npad] == n)[0]
+    rng = np.random.default_rng(0)
+    if rows.size > 192:
+        rows = np.sort(rng.choice(rows, 192, replace=False))
+    act = b.act
+    # pad rows of act are zero
+    if pads.size:
+        assert not _f64(act[torch.from_numpy(pads).cuda()]).any()
+    x64 = synth.bf16_to_f64(inp.x)
+    act_ref, act_gpu, y_ref, y_gpu = [], [], [], []
+    for r in rows:
+        i = int(sorted_ids[r])
+        t, e = i // s.k, int(block_expert[r // b.block_m])
+        act_ref.append(oracle.expert_gate_up(x64[t], inp.w13[e])[0])
+        a_gpu = _f64(act[r])
+        act_gpu.append(a_gpu)
+        y_ref.append(oracle.expert_down(a_gpu, inp.w2[e])[0])
+        y_gpu.append(_f64(b.y[i]))
+    elem_close(np.array(act_gpu), np.array(act_ref), what="gate_up act")
+    elem_close(np.array(y_gpu), np.array(y_ref), what="down y")
+    # combine: fp32 output against the oracle's weighted sum of the GPU's y
+    toks = sample_tokens(s.T, 128)
+    out32 = torch.empty((s.T, s.H), dtype=torch.float32, device="cuda")
+    moe.moe_combine(b.y, b.topk_weights, s.T, s.k, s.H, out32)
+    torch.cuda.synchronize()
+    y3 = _f64(b.y).reshape(s.T, s.k, s.H)[toks]
+    w3 = b.topk_weights.cpu().numpy().astype(np.float64)[toks]
+    ref = oracle.combine(y3, w3)
+    tol = (s.k + 1) * 2.0 ** -23 * (np.abs(w3)[:, :, None] * np.abs(y3)).sum(1) + 1e-30
+    assert (np.abs(out32.cpu().numpy()[toks] - ref) <= tol).all()
+    elem_close(_f64(out)[toks], ref, rel=2.0 ** -8, floor_frac=1e-6, what="combine bf16")
+
+
+# ----------------------------------------------------------------------------
+# The whole layer
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("name", CONFIG_NAMES)
+def test_layer_matches_oracle(name):
+    log(f"layer {name}")
+    inp = host_inputs(name)
+    s = inp.shape
+    dev = device_inputs(inp, key=name)
+    out, b = run_layer(inp, dev)
+    toks = sample_tokens(s.T, 96)
+    ref, ref_ids, ref_w = oracle.moe_layer(inp.x, inp.w_router, inp.w13, inp.w2, s.k, s.norm_topk_prob,
+                                           inp.router_bias, toks)
+    got = _f64(out)[toks]
+    assert np.isfinite(got).all()
+    assert np.array_equal(b.topk_ids.cpu().numpy()[toks], ref_ids)
+    assert np.abs(b.topk_weights.cpu().numpy()[toks] - ref_w).max() <= 1e-6
+    err = np.abs(got - ref).max()
+    tol = layer_tolerance(ref)
+    log(f"  {name}: max err {err:.3e}, bound {tol:.3e}, rms {np.sqrt(np.mean(ref ** 2)):.3e}")
+    assert err <= tol
+    if name == "tiny":
+        assert err <= layer_tolerance(ref, floor=False)
+
+
+def test_layer_edge_cases():
+    cases = [
+        ("one_token", 1, 256, 16, 4, 64, True),
+        ("ragged", 37, 128, 8, 2, 96, True),
+        ("dense", 45, 128, 1, 1, 64, True),
+        ("k_eq_E", 20, 64, 8, 8, 32, False),
+        ("wide", 33, 64, 256, 32, 32, True),
+        ("no_renorm", 50, 192, 12, 3, 160, False),
+        ("multi_tile", 600, 64, 16, 8, 64, True),
+    ]
+    for name, T, H, E, k, I, norm in cases:
+        log(f"edge {name}")
+        inp = custom_inputs(name, T, H, E, k, I, norm=norm, seed=T)
+        out, b = run_layer(inp)
+        ref, ref_ids, _ = oracle.moe_layer(inp.x, inp.w_router, inp.w13, inp.w2, k, norm)
+        assert np.array_equal(b.topk_ids.cpu().numpy(), ref_ids), name
+        err = np.abs(_f64(out) - ref).max()
+        assert err <= layer_tolerance(ref), (name, err)
+
+
+def test_zero_tokens_is_a_noop():
+    inp = custom_inputs("empty", 4, 64, 8, 2, 32)
+    dev = device_inputs(inp)
+    out = torch.full((0, 64), 3.0, dtype=torch.bfloat16, device="cuda")
+    x0 = dev["x"][:0]
+    res = moe.moe_layer(x0, dev["w_router"], dev["w13"], dev["w2"], top_k=2)
+    torch.cuda.synchronize()
+    assert res.shape == (0, 64) and out.shape == (0, 64)
+
+
+# ----------------------------------------------------------------------------
+# Structure: poisoning, determinism, batch split, relabelling, tile size
+# ----------------------------------------------------------------------------
+def test_nan_poison_unused_experts_and_pad_rows():
+    inp = custom_inputs("poison", 300, 256, 32, 4, 128, skewed=True, seed=3)
+    s = inp.shape
+    clean, bc = run_layer(inp, block_m=32)
+    counts = bc.expert_counts.cpu().numpy()
+    unused = np.nonzero(counts == 0)[0]
+    assert unused.size >= 5
+    w13p, w2p = inp.w13.copy(), inp.w2.copy()
+    w13p[unused] = NAN_BF16
+    w2p[unused] = NAN_BF16
+    dev = device_inputs(inp)
+    dev = dict(dev, w13=bf16_tensor(w13p), w2=bf16_tensor(w2p))
+    out, b = run_layer(inp, dev, block_m=32)
+    assert np.array_equal(to_bits(out), to_bits(clean))
+    # poison pad rows of act between the two GEMMs
+    n = s.T * s.k
+    pad = torch.from_numpy(np.nonzero(b.sorted_ids.cpu().numpy() == n)[0]).cuda()
+    b.act[pad] = float("nan")
+    moe.moe_grouped_gemm_down(b.act, dev["w2"], b.sorted_ids, b.block_expert, b.num_padded, s.T, s.k, s.H, s.I, s.E,
+                              b.block_m, b.cap, b.y)
+    out2 = torch.empty_like(out)
+    moe.moe_combine(b.y, b.topk_weights, s.T, s.k, s.H, out2)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out2.float()).all()
+    assert np.array_equal(to_bits(out2), to_bits(clean))
+
+
+@pytest.mark.parametrize("name", ["decode", "prefill"])
+def test_run_twice_bit_identical(name):
+    inp = host_inputs(name)
+    dev = device_inputs(inp, key=name)
+    o1, b1 = run_layer(inp, dev)
+    o2, b2 = run_layer(inp, dev)
+    for f in ("topk_ids", "sorted_ids", "block_expert", "expert_counts", "num_padded"):
+        assert torch.equal(getattr(b1, f), getattr(b2, f)), f
+    for f in ("logits", "topk_weights"):
+        assert torch.equal(getattr(b1, f), getattr(b2, f)), f
+    npad = int(b1.num_padded.item())
+    assert np.array_equal(to_bits(b1.act[:npad]), to_bits(b2.act[:npad]))
+    assert np.array_equal(to_bits(b1.y), to_bits(b2.y))
+    assert np.array_equal(to_bits(o1), to_bits(o2))
+
+
+def test_batch_split_bit_identical():
+    inp = host_inputs("prefill")
+    s = inp.shape
+    dev = device_inputs(inp, key="prefill")
+    full, _ = run_layer(inp, dev, block_m=64)
+    half = s.T // 2
+    sub = synth.MoEInputs(s.with_tokens(half), 0, inp.x[:half], inp.w_router, inp.w13, inp.w2, inp.router_bias)
+    dsub = dict(dev, x=dev["x"][:half].contiguous())
+    part, _ = run_layer(sub, dsub, block_m=64)
+    assert np.array_equal(to_bits(part), to_bits(full[:half]))
+
+
+def test_expert_relabelling_bit_identical():
+    inp = custom_inputs("relabel", 700, 256, 24, 4, 128, seed=5)
+    out, _ = run_layer(inp, block_m=16)
+    perm = np.random.default_rng(2).permutation(24)
+    p = synth.MoEInputs(inp.shape, 5, inp.x, inp.w_router[perm], inp.w13[perm], inp.w2[perm], None)
+    out_p, _ = run_layer(p, block_m=16)
+    assert np.array_equal(to_bits(out_p), to_bits(out))
+
+
+def test_block_m_does_not_change_results():
+    inp = custom_inputs("tiles", 900, 512, 16, 4, 256, seed=9)
+    outs = [to_bits(run_layer(inp, block_m=bm)[0]) for bm in (16, 32, 64, 128)]
+    for o in outs[1:]:
+        assert np.array_equal(o, outs[0])
+
+
+def test_python_errors_on_gpu():
+    inp = custom_inputs("err", 8, 64, 8, 2, 32)
+    dev = device_inputs(inp)
+    with pytest.raises(moe.MoEError, match="k="):
+        moe.moe_layer(dev["x"], dev["w_router"], dev["w13"], dev["w2"], top_k=9)
+    with pytest.raises(ValueError, match="shape mismatch"):
+        moe.moe_layer(dev["x"], dev["w_router"], dev["w2"], dev["w2"], top_k=2)

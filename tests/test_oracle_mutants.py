@@ -27,7 +27,9 @@ MUTANTS = [
     ("down_term_dropped", "for (int64_t i = 0; i < I; ++i) s += act[i] * bf16_value(w2[h * I + i]);",
      "for (int64_t i = 1; i < I; ++i) s += act[i] * bf16_value(w2[h * I + i]);"),
     ("router_transposed", "bf16_value(wr[e * H + h])", "bf16_value(wr[h * E + e])"),
-    ("combine_wrong_slot", "o[h] += w[j] * y[h];", "o[h] += w[0] * y[h];"),
+    ("combine_wrong_slot", "out[h] += w[j] * y[j * H + h];", "out[h] += w[0] * y[j * H + h];"),
+    ("combine_dropped_slot", "for (int64_t j = 0; j < k; ++j)\n        for (int64_t h = 0; h < H; ++h) out[h]",
+     "for (int64_t j = 1; j < k; ++j)\n        for (int64_t h = 0; h < H; ++h) out[h]"),
     ("router_token_zero", "oracle_router_logits(x + t * H, wr, bias, 1, H, E, logits);",
      "oracle_router_logits(x, wr, bias, 1, H, E, logits);"),
     ("align_unstable", "for (int64_t i = 0; i < n; ++i)\n            if (ids[i] == e) sorted_ids[fill++] = (int32_t)i;",
