@@ -24,7 +24,9 @@
  * The layer is five calls, in this order, on one stream:
  *   moe_route -> moe_align_by_expert -> moe_grouped_gemm_gate_up_silu ->
  *   moe_grouped_gemm_down -> moe_combine
- * No residual is added (the decoder adds it outside the MLP).
+ * No residual is added (the decoder adds it outside the MLP). The expert
+ * weights are converted once, when they are loaded, by moe_pack_weights into
+ * the layout the grouped GEMMs stream.
  *
  * Conventions for every call
  *  - Pointers named as device pointers must point to device memory of the
@@ -133,6 +135,30 @@ int moe_align_by_expert(const int32_t* topk_ids, int64_t T, int32_t k, int32_t E
                         int32_t* sorted_ids, int32_t* block_expert, int32_t* expert_counts, int32_t* num_padded,
                         void* workspace, size_t workspace_bytes, void* stream);
 
+/* Bytes of a packed [E, N, K] bf16 weight (equal to the row-major size), or
+ * 0 when the shape cannot be packed (needs N % 16 == 0 and K % 32 == 0). */
+size_t moe_packed_weight_bytes(int32_t E, int32_t N, int32_t K);
+
+/*
+ * Convert expert weights from the row-major layout they are loaded in
+ * ([Models], "Streaming weight loading": per-expert tensors stacked into
+ * [E, N, K]) into the fragment layout the grouped GEMMs read. Done once per
+ * weight, outside the layer.
+ *
+ *   w         [E, N, K] bf16, device, row-major. For the merged gate/up
+ *             weight (gated != 0) N = 2I with rows 0..I-1 gate and I..2I-1
+ *             up; for the down weight (gated == 0) N = H, K = I.
+ *   w_packed  device buffer of moe_packed_weight_bytes(E, N, K) bytes,
+ *             output; must not overlap w.
+ * Layout of w_packed: each expert's rows are cut into 16-row bands and each
+ * band into 32-column k-steps; block (band, k-step) is 512 contiguous bf16 in
+ * which elements 8l..8l+7 hold row l%16 of the band at columns 8*(l/16) ..
+ * 8*(l/16)+7 of the k-step (l = 0..63). Blocks are ordered expert, band,
+ * k-step. When gated, packed band 2b is gate band b (rows 16b..16b+15) and
+ * packed band 2b+1 is up band b (rows I+16b..I+16b+15).
+ */
+int moe_pack_weights(const void* w, void* w_packed, int32_t E, int32_t N, int32_t K, int32_t gated, void* stream);
+
 /*
  * Grouped gate/up projection with fused SiLU-and-mul ([Models], "Model
  * structure": gate_up_proj, then silu(gate) * up). For every row r below
@@ -144,7 +170,10 @@ int moe_align_by_expert(const int32_t* topk_ids, int64_t T, int32_t k, int32_t E
  * written as zeros. Rows from num_padded on are not touched.
  *
  *   x          [T, H] bf16, device.
- *   w13        [E, 2I, H] bf16, device: rows 0..I-1 gate, I..2I-1 up.
+ *   w13        [E, 2I, H] bf16, device, packed by moe_pack_weights (gated = 1)
+ *              from the row-major weight whose rows 0..I-1 are gate and
+ *              I..2I-1 up; w13[e, c, h] above refers to that row-major
+ *              weight.
  *   sorted_ids, block_expert, num_padded: from moe_align_by_expert with the
  *              same T, k, E, block_m; cap = moe_align_capacity(...).
  *   act        [cap, I] bf16, device, output (rows in sorted order).
@@ -158,13 +187,16 @@ int moe_grouped_gemm_gate_up_silu(const void* x, const void* w13, const int32_t*
  * Grouped down projection ([Models], "Model structure": down_proj). For
  * every row r below num_padded with sorted_ids[r] = i not the sentinel and
  * e = block_expert[r / block_m]:
- *   y[i, h] = bf16(sum_c act[r, c] * w2[e, h, c])
- * (fp32 accumulation). Every one of the T*k rows of y is written exactly
- * once; pad rows of act are never used for a real row.
+ *   y[i, h] = sum_c act[r, c] * w2[e, h, c]
+ * accumulated and stored in fp32 (keeping y in fp32 keeps the layer's
+ * error dominated by the final bf16 rounding of the output). Every one of
+ * the T*k rows of y is written exactly once; pad rows of act are never used
+ * for a real row.
  *
  *   act  [cap, I] bf16, device (from moe_grouped_gemm_gate_up_silu).
- *   w2   [E, H, I] bf16, device.
- *   y    [T*k, H] bf16, device, output, in (token, slot) order.
+ *   w2   [E, H, I] bf16, device, packed by moe_pack_weights (gated = 0);
+ *        w2[e, h, c] above refers to the row-major weight.
+ *   y    [T*k, H] fp32, device, output, in (token, slot) order.
  */
 int moe_grouped_gemm_down(const void* act, const void* w2, const int32_t* sorted_ids, const int32_t* block_expert,
                           const int32_t* num_padded, int64_t T, int32_t k, int32_t H, int32_t I, int32_t E,
@@ -175,7 +207,7 @@ int moe_grouped_gemm_down(const void* act, const void* w2, const int32_t* sorted
  * weighted by their scores and summed):
  *   out[t, h] = sum_j topk_weights[t, j] * y[t*k + j, h]   (fp32 accumulation)
  *
- *   y             [T*k, H] bf16, device.
+ *   y             [T*k, H] fp32, device.
  *   topk_weights  [T, k] fp32, device.
  *   out           [T, H], device: bf16 (round to nearest even) when
  *                 out_dtype == MOE_OUT_BF16, fp32 when MOE_OUT_FP32.

@@ -24,7 +24,9 @@ from ._lib import (  # noqa: F401
     moe_grouped_gemm_down,
     moe_grouped_gemm_gate_up_silu,
     moe_last_error,
+    moe_pack_weights,
+    moe_packed_weight_bytes,
     moe_pick_block_m,
     moe_route,
 )
-from .layer import MoEBuffers, MoEConfig, allocate, moe_layer  # noqa: F401
+from .layer import MoEBuffers, MoEConfig, PackedExperts, allocate, moe_layer, pack_experts  # noqa: F401

@@ -37,6 +37,8 @@ EXPORTS = (
     "moe_grouped_gemm_down",
     "moe_combine",
     "moe_pick_block_m",
+    "moe_packed_weight_bytes",
+    "moe_pack_weights",
 )
 
 
@@ -71,6 +73,8 @@ def lib():
         L.moe_grouped_gemm_down.argtypes = [p, p, p, p, p, i64, i32, i32, i32, i32, i32, i64, p, p]
         L.moe_combine.argtypes = [p, p, i64, i32, i32, p, i32, p]
         L.moe_pick_block_m.argtypes, L.moe_pick_block_m.restype = [i64, i32, i32], i32
+        L.moe_packed_weight_bytes.argtypes, L.moe_packed_weight_bytes.restype = [i32, i32, i32], sz
+        L.moe_pack_weights.argtypes, L.moe_pack_weights.restype = [p, p, i32, i32, i32, i32, p], ctypes.c_int
         for name in ("moe_route", "moe_align_by_expert", "moe_grouped_gemm_gate_up_silu", "moe_grouped_gemm_down",
                      "moe_combine"):
             getattr(L, name).restype = ctypes.c_int
@@ -144,6 +148,17 @@ def moe_pick_block_m(T: int, k: int, E: int) -> int:
     return lib().moe_pick_block_m(T, k, E)
 
 
+def moe_packed_weight_bytes(E: int, N: int, K: int) -> int:
+    return lib().moe_packed_weight_bytes(E, N, K)
+
+
+def moe_pack_weights(w, w_packed, E: int, N: int, K: int, gated: bool, stream=None):
+    """Row-major [E, N, K] bf16 -> the GEMMs' fragment layout (same size)."""
+    bf = torch.bfloat16
+    _check(lib().moe_pack_weights(_dev(w, bf, "w"), _dev(w_packed, bf, "w_packed"), E, N, K, int(bool(gated)),
+                                  _stream(stream, w)))
+
+
 def moe_align_by_expert(topk_ids, T: int, k: int, E: int, block_m: int, sorted_ids, block_expert, expert_counts,
                         num_padded, workspace=None, stream=None):
     i32 = torch.int32
@@ -173,7 +188,8 @@ def moe_grouped_gemm_down(act, w2, sorted_ids, block_expert, num_padded, T: int,
     bf, i32 = torch.bfloat16, torch.int32
     _check(lib().moe_grouped_gemm_down(_dev(act, bf, "act"), _dev(w2, bf, "w2"), _dev(sorted_ids, i32, "sorted_ids"),
                                        _dev(block_expert, i32, "block_expert"), _dev(num_padded, i32, "num_padded"),
-                                       T, k, H, I, E, block_m, cap, _dev(y, bf, "y"), _stream(stream, act)))
+                                       T, k, H, I, E, block_m, cap, _dev(y, torch.float32, "y"),
+                                       _stream(stream, act)))
 
 
 def moe_combine(y, topk_weights, T: int, k: int, H: int, out, stream=None):
@@ -181,5 +197,5 @@ def moe_combine(y, topk_weights, T: int, k: int, H: int, out, stream=None):
     if out is None or out.dtype not in (torch.bfloat16, torch.float32):
         raise TypeError("out must be a bf16 or fp32 tensor")
     od = MOE_OUT_FP32 if out.dtype == torch.float32 else MOE_OUT_BF16
-    _check(lib().moe_combine(_dev(y, torch.bfloat16, "y"), _dev(topk_weights, torch.float32, "topk_weights"), T, k, H,
+    _check(lib().moe_combine(_dev(y, torch.float32, "y"), _dev(topk_weights, torch.float32, "topk_weights"), T, k, H,
                              _dev(out, out.dtype, "out"), od, _stream(stream, y)))

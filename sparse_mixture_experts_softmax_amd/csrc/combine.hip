@@ -1,8 +1,8 @@
-// moe_combine: out[t, :] = sum_j w[t, j] * y[t*k + j, :] in fp32.
+// moe_combine: out[t, :] = sum_j w[t, j] * y[t*k + j, :] in fp32 (y is fp32).
 //
 // The k rows of a token are adjacent in y (token, slot order), so each
-// thread streams 16-byte chunks (8 bf16) of those rows and of the output
-// row: fully coalesced, HBM-bound. One workgroup per token, 256 threads; a
+// thread streams two 16-byte chunks (8 fp32) of those rows and writes 8
+// outputs: fully coalesced, HBM-bound. One workgroup per token, 256 threads; a
 // thread covers hidden positions 8*tid + 2048*m.
 #include "abi_util.h"
 #include "moe_common.h"
@@ -12,11 +12,11 @@ namespace moe {
 constexpr int kCombineThreads = 256;
 
 template <bool OUT_F32>
-__global__ __launch_bounds__(kCombineThreads) void combine_kernel(const uint16_t* __restrict__ y,
+__global__ __launch_bounds__(kCombineThreads) void combine_kernel(const float* __restrict__ y,
                                                                   const float* __restrict__ w, int k, int H,
                                                                   void* __restrict__ out) {
     const int64_t t = blockIdx.x;
-    const uint16_t* yt = y + t * k * (int64_t)H;
+    const float* yt = y + t * k * (int64_t)H;
     const float* wt = w + t * k;
     for (int h = threadIdx.x * 8; h < H; h += kCombineThreads * 8) {
         float acc[8];
@@ -24,11 +24,12 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const uint16_t
         for (int q = 0; q < 8; ++q) acc[q] = 0.f;
         for (int j = 0; j < k; ++j) {
             const float wj = wt[j];
-            const u32x4 v = *(const u32x4*)(yt + (int64_t)j * H + h);
+            const f32x4 v0 = *(const f32x4*)(yt + (int64_t)j * H + h);
+            const f32x4 v1 = *(const f32x4*)(yt + (int64_t)j * H + h + 4);
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                acc[2 * q] += wj * __uint_as_float(v[q] << 16);
-                acc[2 * q + 1] += wj * __uint_as_float(v[q] & 0xffff0000u);
+                acc[q] += wj * v0[q];
+                acc[4 + q] += wj * v1[q];
             }
         }
         if (OUT_F32) {
@@ -63,9 +64,9 @@ extern "C" int moe_combine(const void* y, const float* topk_weights, int64_t T, 
     if (T >= ((int64_t)1 << 31)) return set_error(MOE_ERR_UNSUPPORTED, "moe_combine: T too large");
     if (out_dtype == MOE_OUT_FP32)
         hipLaunchKernelGGL(combine_kernel<true>, dim3((unsigned)T), dim3(kCombineThreads), 0, (hipStream_t)stream,
-                           (const uint16_t*)y, topk_weights, (int)k, (int)H, out);
+                           (const float*)y, topk_weights, (int)k, (int)H, out);
     else
         hipLaunchKernelGGL(combine_kernel<false>, dim3((unsigned)T), dim3(kCombineThreads), 0, (hipStream_t)stream,
-                           (const uint16_t*)y, topk_weights, (int)k, (int)H, out);
+                           (const float*)y, topk_weights, (int)k, (int)H, out);
     return check_launch("moe_combine");
 }

@@ -2,21 +2,26 @@
 // accumulation), one launch for all experts.
 //
 //   gate/up:  act[r, c] = silu(x[t] . w13[e, c]) * (x[t] . w13[e, I + c])
-//   down:     y[i, h]   = act[r] . w2[e, h]
+//   down:     y[i, h]   = act[r] . w2[e, h]      (y kept in fp32)
 //
 // with r a row of the expert-grouped permutation, i = sorted_ids[r] the flat
 // (token, slot) index, t = i / k its token and e = block_expert[r / BM] the
-// expert owning the row block. Both operands are K-contiguous (x rows / act
-// rows and weight rows), so A and B fragments load the same way.
+// expert owning the row block. Activations are row-major; weights come in
+// the fragment layout of moe_pack_weights (16-row bands x 32-column k-steps,
+// each a contiguous 1 KB MFMA B operand; gate and up bands interleaved), so
+// every weight load instruction reads 1 KB contiguous.
 //
 // Grid: one workgroup per (row block, N tile), row-block major; blocks past
 // num_padded (read on the device) return at once, so no host sync is needed.
-// Each workgroup stages BMxBK activation rows (gathered through sorted_ids
-// for gate/up) and BNxBK weight rows in LDS with 16-byte coalesced loads,
-// double-buffered: the next K tile is loaded into registers while the
-// current one feeds the MFMAs. For gate/up an N tile holds BN/2 gate rows and
-// the BN/2 matching up rows, so each wave owns the gate and up accumulators
-// of the same output columns and applies silu(g) * u in registers.
+//
+// General kernel (row blocks of 32..128): each workgroup stages BMxBK
+// activation rows (gathered through sorted_ids for gate/up) in padded
+// row-major LDS and the tile's BN/16 weight bands (BK/32 fragments each) in
+// fragment-major LDS, double-buffered: the next K tile is loaded into
+// registers while the current one feeds the MFMAs. For gate/up an N tile
+// holds BN/2 gate rows and the BN/2 matching up rows, so each wave owns the
+// gate and up accumulators of the same output columns and applies
+// silu(g) * u in registers.
 #include "abi_util.h"
 #include "moe_common.h"
 
@@ -36,7 +41,8 @@ struct GemmCfg {
     static constexpr int WTN = BN / WAVES_N;
     static constexpr int MT = WTM / 16;
     static constexpr int NT = WTN / 16;
-    static constexpr int STRIDE = BK + 8;  // LDS row stride in elements (16-byte pad)
+    static constexpr int STRIDE = BK + 8;  // A: LDS row stride in elements (16-byte pad)
+    static constexpr int KS = BK / 32;     // k-steps (fragments per band) per K tile
     static constexpr int A_CHUNKS = BM * BK / 8;
     static constexpr int B_CHUNKS = BN * BK / 8;
     static constexpr int A_PER_T = (A_CHUNKS + THREADS - 1) / THREADS;
@@ -49,10 +55,10 @@ template <class C>
 __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(
     const uint16_t* __restrict__ a_src, const uint16_t* __restrict__ w, const int32_t* __restrict__ sorted_ids,
     const int32_t* __restrict__ block_expert, const int32_t* __restrict__ num_padded, int k, int64_t n_pairs,
-    int K, int N_out, int n_tiles, uint16_t* __restrict__ out) {
+    int K, int N_out, int n_tiles, void* __restrict__ out) {
     constexpr int BM = C::BM, BN = C::BN, BK = C::BK, STRIDE = C::STRIDE;
     __shared__ __attribute__((aligned(16))) uint16_t sA[2][BM * STRIDE];
-    __shared__ __attribute__((aligned(16))) uint16_t sB[2][BN * STRIDE];
+    __shared__ __attribute__((aligned(16))) uint16_t sB[2][BN * BK];  // [band][k-step][512]
     __shared__ int64_t row_src[BM];  // gate/up: x row offset (-1 = zero row); down: y row (-1 = skip)
 
     const int tid = threadIdx.x;
@@ -88,43 +94,39 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(
             a_ok[j] = a_ok[j] && src >= 0;
             a_ptr[j] = a_src + (src >= 0 ? src : 0) + kc;
         } else {
-            a_ptr[j] = a_src + ((int64_t)mb * BM + row) * K + kc;
+            a_ptr[j] = a_src + ((int64_t)mb * BM + (a_ok[j] ? row : 0)) * K + kc;
         }
     }
+    // B chunk c of a K tile: band-in-tile c / (KS*64), k-step (c / 64) % KS,
+    // lane c % 64. Bands past the weight (ragged N) are clamped to the last
+    // band: their columns are never stored.
+    const int bands = (int)(w_rows / 16);
+    const int ksteps = K / 32;
     const uint16_t* b_ptr[C::B_PER_T];
-    bool b_ok[C::B_PER_T];
 #pragma unroll
     for (int j = 0; j < C::B_PER_T; ++j) {
-        const int c = tid + j * C::THREADS;
-        const int row = c / (BK / 8), kc = (c % (BK / 8)) * 8;
-        int64_t wrow;
-        bool ok = c < C::B_CHUNKS;
-        if (C::GATED) {
-            const int half = BN / 2;
-            const int col = tn * half + (row % half);  // output column this weight row feeds
-            ok = ok && col < N_out;
-            wrow = (row < half) ? col : (int64_t)N_out + col;
-        } else {
-            const int col = tn * BN + row;
-            ok = ok && col < N_out;
-            wrow = col;
-        }
-        b_ok[j] = ok;
-        b_ptr[j] = we + (ok ? wrow : 0) * K + kc;
+        const int c = min(tid + j * C::THREADS, C::B_CHUNKS - 1);
+        const int band = min(tn * (BN / 16) + c / (C::KS * 64), bands - 1);
+        b_ptr[j] = we + (int64_t)band * 16 * K + ((c / 64) % C::KS) * 512 + (c % 64) * 8;
     }
 
+    // Unconditional loads from clamped addresses; values outside the operand
+    // (sentinel rows, the K tail) are zeroed with sel(). B rows past N_out
+    // are clamped to row 0: their columns are never stored.
     u32x4 ra[C::A_PER_T], rb[C::B_PER_T];
     auto load_tile = [&](int kt) {
         const int k0 = kt * BK;
 #pragma unroll
         for (int j = 0; j < C::A_PER_T; ++j) {
             const int kc = ((tid + j * C::THREADS) % (BK / 8)) * 8;
-            ra[j] = (a_ok[j] && k0 + kc < K) ? *(const u32x4*)(a_ptr[j] + k0) : u32x4{0u, 0u, 0u, 0u};
+            const bool in = k0 + kc < K;
+            ra[j] = sel(a_ok[j] && in, ld16(a_ptr[j] + (in ? k0 : 0)));
         }
 #pragma unroll
         for (int j = 0; j < C::B_PER_T; ++j) {
-            const int kc = ((tid + j * C::THREADS) % (BK / 8)) * 8;
-            rb[j] = (b_ok[j] && k0 + kc < K) ? *(const u32x4*)(b_ptr[j] + k0) : u32x4{0u, 0u, 0u, 0u};
+            const int ks = ((tid + j * C::THREADS) / 64) % C::KS;
+            const bool in = kt * C::KS + ks < ksteps;
+            rb[j] = sel(in, ld16(b_ptr[j] + (in ? kt * C::KS * 512 : 0)));
         }
     };
     auto store_tile = [&](int buf) {
@@ -136,7 +138,7 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(
 #pragma unroll
         for (int j = 0; j < C::B_PER_T; ++j) {
             const int c = tid + j * C::THREADS;
-            if (c < C::B_CHUNKS) *(u32x4*)&sB[buf][(c / (BK / 8)) * STRIDE + (c % (BK / 8)) * 8] = rb[j];
+            if (c < C::B_CHUNKS) *(u32x4*)&sB[buf][c * 8] = rb[j];
         }
     };
 
@@ -147,14 +149,16 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(
 #pragma unroll
         for (int j = 0; j < C::NT; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // LDS row of B that wave-tile column block j reads
-    auto b_lds_row = [&](int j) {
+    // band (within the N tile) that wave-tile column block j reads: gate/up
+    // bands are interleaved, so gate tile g of output columns c.. is band
+    // 2*(c/16) and its up tile the next band
+    auto b_band = [&](int j) {
         if (C::GATED) {
             constexpr int HALF_NT = C::NT / 2;
             const int g = j % HALF_NT;
-            return (j < HALF_NT ? 0 : BN / 2) + wn * (C::WTN / 2) + g * 16;
+            return 2 * (wn * (C::WTN / 32) + g) + (j < HALF_NT ? 0 : 1);
         }
-        return wn * C::WTN + j * 16;
+        return wn * (C::WTN / 16) + j;
     };
 
     const int nk = (K + BK - 1) / BK;
@@ -172,7 +176,7 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(
             for (int i = 0; i < C::MT; ++i)
                 fa[i] = *(const u32x4*)&sA[buf][(wm * C::WTM + i * 16 + lane % 16) * STRIDE + kof];
 #pragma unroll
-            for (int j = 0; j < C::NT; ++j) fb[j] = *(const u32x4*)&sB[buf][(b_lds_row(j) + lane % 16) * STRIDE + kof];
+            for (int j = 0; j < C::NT; ++j) fb[j] = *(const u32x4*)&sB[buf][(b_band(j) * C::KS + ks) * 512 + lane * 8];
 #pragma unroll
             for (int i = 0; i < C::MT; ++i)
 #pragma unroll
@@ -195,7 +199,7 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(
                 for (int q = 0; q < 4; ++q) {
                     const int row = wm * C::WTM + i * 16 + (lane / 16) * 4 + q;
                     const float v = silu(acc[i][g][q]) * acc[i][g + HALF_NT][q];
-                    out[((int64_t)mb * BM + row) * N_out + col] = f32_to_bf16(v);
+                    ((uint16_t*)out)[((int64_t)mb * BM + row) * N_out + col] = f32_to_bf16(v);
                 }
             }
         }
@@ -210,11 +214,149 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(
                 for (int q = 0; q < 4; ++q) {
                     const int row = wm * C::WTM + i * 16 + (lane / 16) * 4 + q;
                     const int64_t dst = row_src[row];
-                    if (dst >= 0) out[dst * N_out + col] = f32_to_bf16(acc[i][j][q]);
+                    if (dst >= 0) ((float*)out)[dst * N_out + col] = acc[i][j][q];
                 }
             }
         }
     }
+}
+
+// Skinny variant for 16-row blocks (a handful of rows per expert, as in
+// decode): the work is streaming each touched expert's weights once, so the
+// weights bypass LDS. Each wave owns NTILE packed 16-row bands (gate/up:
+// NTILE/2 gate bands and the NTILE/2 matching up bands, i.e. 8*NTILE output
+// columns; down: NTILE bands, 16*NTILE output columns) and streams them from
+// HBM straight into MFMA B-fragments, 1 KB contiguous per load, U k-steps per
+// stage, two stages in flight. The gathered activation rows (A-fragments) are re-read from L2
+// (the activation matrix is small in this regime).
+template <bool GATED, int NW, int NTILE, int U>
+__global__ __launch_bounds__(NW* kWave) void grouped_gemm_skinny_kernel(
+    const uint16_t* __restrict__ a_src, const uint16_t* __restrict__ w, const int32_t* __restrict__ sorted_ids,
+    const int32_t* __restrict__ block_expert, const int32_t* __restrict__ num_padded, int k, int64_t n_pairs,
+    int K, int N_out, int n_tiles, void* __restrict__ out) {
+    constexpr int BM = 16;
+    constexpr int COLS = GATED ? 8 * NTILE : 16 * NTILE;  // output columns per wave
+    static_assert(!GATED || NTILE % 2 == 0, "gate/up needs gate and up tiles in pairs");
+    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+    const int mb = blockIdx.x / n_tiles;
+    const int tn = blockIdx.x % n_tiles;
+    if ((int64_t)mb * BM >= (int64_t)*num_padded) return;
+    const int e = block_expert[mb];
+    if (e < 0) return;
+    const int64_t w_rows = GATED ? 2 * (int64_t)N_out : (int64_t)N_out;
+    const uint16_t* we = w + (int64_t)e * w_rows * K;
+    const int c0 = (tn * NW + wave) * COLS;  // first output column of this wave
+    const int r16 = lane % 16, koff = (lane / 16) * 8;
+
+    // A: row r16 of the block
+    const int32_t id = sorted_ids[(int64_t)mb * BM + r16];
+    const bool a_ok = id >= 0 && (int64_t)id < n_pairs;
+    const uint16_t* ap;
+    if (GATED) ap = a_src + (a_ok ? (int64_t)(id / k) * K : 0) + koff;  // sentinel -> row 0, zeroed
+    else ap = a_src + ((int64_t)mb * BM + r16) * K + koff;
+    const bool a_live = GATED ? a_ok : true;
+
+    // B: NTILE packed bands of 16 weight rows (gate/up: gate band 2c, up
+    // band 2c+1 for output columns 16c..16c+15). Bands past the weight are
+    // clamped to the last band: their columns are never stored.
+    const int bands = (int)(w_rows / 16);
+    const uint16_t* bp[NTILE];
+#pragma unroll
+    for (int j = 0; j < NTILE; ++j) {
+        int band;
+        if (GATED) band = 2 * (c0 / 16 + j % (NTILE / 2)) + (j < NTILE / 2 ? 0 : 1);
+        else band = c0 / 16 + j;
+        bp[j] = we + (int64_t)min(band, bands - 1) * 16 * K + lane * 8;
+    }
+
+    f32x4 acc[NTILE];
+#pragma unroll
+    for (int j = 0; j < NTILE; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    u32x4 ra[2][U], rb[2][NTILE][U];
+    // Loads are unconditional: rows outside the operand were clamped to a
+    // valid row above (their columns are never stored) and sentinel A rows
+    // are zeroed by sel() so pad rows of act come out as zeros.
+    auto load = [&](int st, int s0) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int kk = (s0 + u) * 32;
+            ra[st][u] = sel(a_live, ld16(ap + kk));
+#pragma unroll
+            for (int j = 0; j < NTILE; ++j) rb[st][j][u] = ld16(bp[j] + (s0 + u) * 512);
+        }
+    };
+    auto compute = [&](int st) {
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int j = 0; j < NTILE; ++j) acc[j] = mfma16x16x32(ra[st][u], rb[st][j][u], acc[j]);
+    };
+    const int ksteps = K / 32;
+    const int nstage = ksteps / U;  // full stages; the ksteps % U tail follows
+    if (nstage > 0) load(0, 0);
+    for (int c = 0; c < nstage; c += 2) {
+        if (c + 1 < nstage) load(1, (c + 1) * U);
+        compute(0);
+        if (c + 2 < nstage) load(0, (c + 2) * U);
+        if (c + 1 < nstage) compute(1);
+    }
+    for (int s = nstage * U; s < ksteps; ++s) {
+        const u32x4 a = sel(a_live, ld16(ap + s * 32));
+#pragma unroll
+        for (int j = 0; j < NTILE; ++j) acc[j] = mfma16x16x32(a, ld16(bp[j] + s * 512), acc[j]);
+    }
+
+    // Epilogue: lane holds rows 4*(lane/16)+q, column lane%16 of each tile.
+    if (GATED) {
+#pragma unroll
+        for (int g = 0; g < NTILE / 2; ++g) {
+            const int col = c0 + g * 16 + r16;
+            if (col >= N_out) continue;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int row = (lane / 16) * 4 + q;
+                const float v = silu(acc[g][q]) * acc[g + NTILE / 2][q];
+                ((uint16_t*)out)[((int64_t)mb * BM + row) * N_out + col] = f32_to_bf16(v);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int row = (lane / 16) * 4 + q;
+            const int32_t dst = sorted_ids[(int64_t)mb * BM + row];
+            if (dst < 0 || (int64_t)dst >= n_pairs) continue;
+#pragma unroll
+            for (int j = 0; j < NTILE; ++j) {
+                const int col = c0 + j * 16 + r16;
+                if (col < N_out) ((float*)out)[(int64_t)dst * N_out + col] = acc[j][q];
+            }
+        }
+    }
+}
+
+template <bool GATED, int NW, int NTILE, int U>
+static int launch_skinny_cfg(const void* a, const void* w, const int32_t* sorted_ids, const int32_t* block_expert,
+                             const int32_t* num_padded, int k, int64_t n_pairs, int K, int N_out, int64_t cap,
+                             void* out, hipStream_t s, const char* what) {
+    const int cols_per_wg = NW * (GATED ? 8 * NTILE : 16 * NTILE);
+    const int n_tiles = (N_out + cols_per_wg - 1) / cols_per_wg;
+    const int64_t grid = (cap / 16) * n_tiles;
+    if (grid >= ((int64_t)1 << 31)) return set_error(MOE_ERR_UNSUPPORTED, "%s: grid too large", what);
+    hipLaunchKernelGGL((grouped_gemm_skinny_kernel<GATED, NW, NTILE, U>), dim3((unsigned)grid), dim3(NW * kWave), 0,
+                       s, (const uint16_t*)a, (const uint16_t*)w, sorted_ids, block_expert, num_padded, k, n_pairs, K,
+                       N_out, n_tiles, out);
+    return check_launch(what);
+}
+
+template <bool GATED>
+static int launch_skinny(const void* a, const void* w, const int32_t* sorted_ids, const int32_t* block_expert,
+                         const int32_t* num_padded, int k, int64_t n_pairs, int K, int N_out, int64_t cap, void* out,
+                         hipStream_t s, const char* what) {
+    if (GATED)
+        return launch_skinny_cfg<true, 4, 2, 8>(a, w, sorted_ids, block_expert, num_padded, k, n_pairs, K, N_out, cap,
+                                                out, s, what);
+    return launch_skinny_cfg<false, 4, 4, 4>(a, w, sorted_ids, block_expert, num_padded, k, n_pairs, K, N_out, cap,
+                                             out, s, what);
 }
 
 template <class C>
@@ -228,7 +370,7 @@ static int launch_gemm(const void* a, const void* w, const int32_t* sorted_ids, 
     if (grid >= ((int64_t)1 << 31)) return set_error(MOE_ERR_UNSUPPORTED, "%s: grid too large", what);
     hipLaunchKernelGGL(grouped_gemm_kernel<C>, dim3((unsigned)grid), dim3(C::THREADS), 0, s, (const uint16_t*)a,
                        (const uint16_t*)w, sorted_ids, block_expert, num_padded, k, n_pairs, K, N_out, n_tiles,
-                       (uint16_t*)out);
+                       out);
     return check_launch(what);
 }
 
@@ -238,8 +380,8 @@ static int dispatch_gemm(int32_t block_m, const void* a, const void* w, const in
                          int N_out, int64_t cap, void* out, hipStream_t s, const char* what) {
     switch (block_m) {
         case 16:
-            return launch_gemm<GemmCfg<16, 128, GATED>>(a, w, sorted_ids, block_expert, num_padded, k, n_pairs, K,
-                                                       N_out, cap, out, s, what);
+            return launch_skinny<GATED>(a, w, sorted_ids, block_expert, num_padded, k, n_pairs, K, N_out, cap, out, s,
+                                        what);
         case 32:
             return launch_gemm<GemmCfg<32, 128, GATED>>(a, w, sorted_ids, block_expert, num_padded, k, n_pairs, K,
                                                        N_out, cap, out, s, what);

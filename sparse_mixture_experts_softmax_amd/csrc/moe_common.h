@@ -36,6 +36,15 @@ __device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
 }
 
+// Unconditional 16-byte load. Callers pass an address that is always valid
+// (clamped) and zero the value afterwards with sel() when it lies outside the
+// operand, so the compiler never wraps loads in branches and can keep several
+// of them in flight.
+__device__ __forceinline__ u32x4 ld16(const uint16_t* p) { return *(const u32x4*)p; }
+__device__ __forceinline__ u32x4 sel(bool keep, u32x4 v) {
+    return u32x4{keep ? v[0] : 0u, keep ? v[1] : 0u, keep ? v[2] : 0u, keep ? v[3] : 0u};
+}
+
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
 
 template <typename T>

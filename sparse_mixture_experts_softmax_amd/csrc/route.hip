@@ -15,7 +15,6 @@ namespace moe {
 
 constexpr int kRouteTokens = 16;  // tokens per workgroup (the MFMA M size)
 constexpr int kRouteWaves = 4;
-constexpr int kMaxNTiles = kMaxExperts / 16;
 
 struct ArgMax {
     float v;
@@ -27,6 +26,8 @@ __device__ __forceinline__ ArgMax better(ArgMax a, ArgMax b) {
     return (b.v > a.v || (b.v == a.v && b.i < a.i)) ? b : a;
 }
 
+// NT = 16-expert tiles covered (experts >= E read as zero rows).
+template <int NT>
 __global__ __launch_bounds__(kRouteWaves* kWave) void route_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr, const float* __restrict__ bias,
     float* __restrict__ logits, int32_t* __restrict__ topk_ids, float* __restrict__ topk_w, int64_t T, int H, int E,
@@ -35,36 +36,44 @@ __global__ __launch_bounds__(kRouteWaves* kWave) void route_kernel(
     const int lane = threadIdx.x % kWave;
     const int wave = threadIdx.x / kWave;
     const int64_t t0 = (int64_t)blockIdx.x * kRouteTokens;
-    const int ntiles = (E + 15) / 16;
     float* lg = &part[0][0][0];  // final [16][E] logits reuse the first partial slab
 
     if (compute_logits) {
-        f32x4 acc[kMaxNTiles];
+        f32x4 acc[NT];
 #pragma unroll
-        for (int n = 0; n < kMaxNTiles; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int n = 0; n < NT; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
         const int row = lane % 16;
         const int koff = (lane / 16) * 8;
         const bool row_ok = t0 + row < T;
-        const uint16_t* xrow = x + (t0 + row) * (int64_t)H + koff;
-        const int ksteps = H / 32;
-        for (int s = wave; s < ksteps; s += kRouteWaves) {
-            u32x4 a = row_ok ? *(const u32x4*)(xrow + s * 32) : u32x4{0u, 0u, 0u, 0u};
+        const uint16_t* xrow = x + (row_ok ? (t0 + row) * (int64_t)H : 0) + koff;
+        const uint16_t* wrow[NT];
+        bool e_ok[NT];
 #pragma unroll
-            for (int n = 0; n < kMaxNTiles; ++n) {
-                if (n < ntiles) {
-                    const int e = n * 16 + row;
-                    u32x4 b = e < E ? *(const u32x4*)(wr + (int64_t)e * H + s * 32 + koff) : u32x4{0u, 0u, 0u, 0u};
-                    acc[n] = mfma16x16x32(a, b, acc[n]);
-                }
-            }
+        for (int n = 0; n < NT; ++n) {
+            const int e = n * 16 + row;
+            e_ok[n] = e < E;
+            wrow[n] = wr + (e_ok[n] ? (int64_t)e * H : 0) + koff;
+        }
+        // this wave's contiguous share of the k-steps
+        const int ksteps = H / 32;
+        const int per = (ksteps + kRouteWaves - 1) / kRouteWaves;
+        const int s_lo = wave * per, s_hi = min(ksteps, s_lo + per);
+#pragma unroll 2
+        for (int s = s_lo; s < s_hi; ++s) {
+            // unconditional loads from clamped rows: rows past T are zeroed,
+            // experts past E only feed logits that are never read
+            const u32x4 a = sel(row_ok, ld16(xrow + s * 32));
+            u32x4 b[NT];
+#pragma unroll
+            for (int n = 0; n < NT; ++n) b[n] = ld16(wrow[n] + s * 32);
+#pragma unroll
+            for (int n = 0; n < NT; ++n) acc[n] = mfma16x16x32(a, b[n], acc[n]);
         }
         // D layout: lane holds rows 4*(lane/16)+i, column lane%16 of each tile
 #pragma unroll
-        for (int n = 0; n < kMaxNTiles; ++n) {
-            if (n < ntiles) {
+        for (int n = 0; n < NT; ++n) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) part[wave][(lane / 16) * 4 + i][n * 16 + lane % 16] = acc[n][i];
-            }
+            for (int i = 0; i < 4; ++i) part[wave][(lane / 16) * 4 + i][n * 16 + lane % 16] = acc[n][i];
         }
         __syncthreads();
         // fixed-order reduction over waves, + bias, store logits
@@ -164,7 +173,13 @@ extern "C" int moe_route(const void* x, const void* w_router, const float* route
     if (!logits || !topk_ids || !topk_weights)
         return set_error(MOE_ERR_INVALID, "moe_route: logits/topk_ids/topk_weights must not be NULL");
     const int64_t blocks = (T + kRouteTokens - 1) / kRouteTokens;
-    hipLaunchKernelGGL(route_kernel, dim3((unsigned)blocks), dim3(kRouteWaves * kWave), 0, (hipStream_t)stream,
+    const int ntiles = (E + 15) / 16;
+    auto kern = ntiles <= 1 ? route_kernel<1>
+              : ntiles <= 2 ? route_kernel<2>
+              : ntiles <= 4 ? route_kernel<4>
+              : ntiles <= 8 ? route_kernel<8>
+                            : route_kernel<16>;
+    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(kRouteWaves * kWave), 0, (hipStream_t)stream,
                        (const uint16_t*)x, (const uint16_t*)w_router, router_bias, logits, topk_ids, topk_weights, T,
                        (int)H, (int)E, (int)k, (int)(norm_topk_prob != 0), (int)(x != nullptr));
     return check_launch("moe_route");

@@ -31,6 +31,31 @@ class MoEConfig:
 
 
 @dataclasses.dataclass
+class PackedExperts:
+    """Expert weights in the grouped GEMMs' fragment layout (moe_pack_weights)."""
+
+    w13: torch.Tensor  # packed [E, 2I, H]
+    w2: torch.Tensor  # packed [E, H, I]
+    num_experts: int
+    hidden_size: int
+    intermediate_size: int
+
+
+def pack_experts(w13: torch.Tensor, w2: torch.Tensor, stream=None) -> PackedExperts:
+    """Pack row-major w13 [E, 2I, H] (gate rows, then up rows) and w2 [E, H, I]
+    once, at load time."""
+    E, two_i, H = w13.shape
+    I = two_i // 2
+    if tuple(w2.shape) != (E, H, I):
+        raise ValueError(f"w2 must be [E, H, I] = {(E, H, I)}, got {tuple(w2.shape)}")
+    p13 = torch.empty_like(w13)
+    p2 = torch.empty_like(w2)
+    _lib.moe_pack_weights(w13, p13, E, 2 * I, H, True, stream)
+    _lib.moe_pack_weights(w2, p2, E, H, I, False, stream)
+    return PackedExperts(p13, p2, E, H, I)
+
+
+@dataclasses.dataclass
 class MoEBuffers:
     """Intermediates of one layer call (kept for inspection by tests)."""
 
@@ -68,38 +93,50 @@ def allocate(T: int, H: int, E: int, k: int, I: int, device, block_m: Optional[i
         num_padded=torch.empty((1,), **i32),
         workspace=torch.empty((ws_bytes,), dtype=torch.uint8, device=device) if ws_bytes else None,
         act=torch.empty((cap, I), dtype=torch.bfloat16, device=device),
-        y=torch.empty((T * k, H), dtype=torch.bfloat16, device=device),
+        y=torch.empty((T * k, H), dtype=torch.float32, device=device),
         out=torch.empty((T, H), dtype=out_dtype, device=device),
         block_m=block_m,
         cap=cap,
     )
 
 
-def moe_layer(x: torch.Tensor, w_router: torch.Tensor, w13: torch.Tensor, w2: torch.Tensor, *, top_k: int,
-              norm_topk_prob: bool = True, router_bias: Optional[torch.Tensor] = None,
+def moe_layer(x: torch.Tensor, w_router: torch.Tensor, w13: Optional[torch.Tensor] = None,
+              w2: Optional[torch.Tensor] = None, *, top_k: int, norm_topk_prob: bool = True,
+              router_bias: Optional[torch.Tensor] = None, packed: Optional[PackedExperts] = None,
               block_m: Optional[int] = None, out_dtype=torch.bfloat16, buffers: Optional[MoEBuffers] = None,
               stream=None) -> torch.Tensor:
     """out[T, H] = sparse MoE layer of x[T, H] (no residual).
 
-    x [T, H], w_router [E, H], w13 [E, 2I, H] (gate rows, then up rows),
-    w2 [E, H, I]: bf16 on the GPU; router_bias [E] fp32 or None."""
-    if x.dim() != 2 or w_router.dim() != 2 or w13.dim() != 3 or w2.dim() != 3:
-        raise ValueError("x [T,H], w_router [E,H], w13 [E,2I,H], w2 [E,H,I] expected")
+    x [T, H], w_router [E, H]: bf16 on the GPU; router_bias [E] fp32 or None.
+    Expert weights either as ``packed`` (from pack_experts, the fast path)
+    or as row-major w13 [E, 2I, H] (gate rows, then up rows) and w2 [E, H, I],
+    which are then packed on every call."""
+    if packed is None:
+        if w13 is None or w2 is None:
+            raise ValueError("pass packed=pack_experts(w13, w2) or the row-major w13 and w2")
+        if w13.dim() != 3 or w2.dim() != 3:
+            raise ValueError("w13 [E,2I,H] and w2 [E,H,I] expected")
+        if w13.shape[0] != w2.shape[0] or w13.shape[2] != w2.shape[1] or w13.shape[1] != 2 * w2.shape[2]:
+            raise ValueError(f"shape mismatch: w13 {tuple(w13.shape)}, w2 {tuple(w2.shape)}")
+        packed = pack_experts(w13, w2, stream)
+    if x.dim() != 2 or w_router.dim() != 2:
+        raise ValueError("x [T,H] and w_router [E,H] expected")
     T, H = x.shape
     E = w_router.shape[0]
-    I = w2.shape[2]
-    if w_router.shape[1] != H or tuple(w13.shape) != (E, 2 * I, H) or tuple(w2.shape) != (E, H, I):
+    I = packed.intermediate_size
+    if w_router.shape[1] != H or packed.num_experts != E or packed.hidden_size != H:
         raise ValueError(f"shape mismatch: x {tuple(x.shape)}, w_router {tuple(w_router.shape)}, "
-                         f"w13 {tuple(w13.shape)}, w2 {tuple(w2.shape)}")
+                         f"experts E={packed.num_experts} H={packed.hidden_size} I={I}")
+    w13p, w2p = packed.w13, packed.w2
     k = int(top_k)
     b = buffers if buffers is not None else allocate(T, H, E, k, I, x.device, block_m, out_dtype)
     s = _lib._stream(stream, x)
     _lib.moe_route(x, w_router, router_bias, b.logits, b.topk_ids, b.topk_weights, T, H, E, k, norm_topk_prob, s)
     _lib.moe_align_by_expert(b.topk_ids, T, k, E, b.block_m, b.sorted_ids, b.block_expert, b.expert_counts,
                              b.num_padded, b.workspace, s)
-    _lib.moe_grouped_gemm_gate_up_silu(x, w13, b.sorted_ids, b.block_expert, b.num_padded, T, k, H, I, E, b.block_m,
+    _lib.moe_grouped_gemm_gate_up_silu(x, w13p, b.sorted_ids, b.block_expert, b.num_padded, T, k, H, I, E, b.block_m,
                                        b.cap, b.act, s)
-    _lib.moe_grouped_gemm_down(b.act, w2, b.sorted_ids, b.block_expert, b.num_padded, T, k, H, I, E, b.block_m, b.cap,
+    _lib.moe_grouped_gemm_down(b.act, w2p, b.sorted_ids, b.block_expert, b.num_padded, T, k, H, I, E, b.block_m, b.cap,
                                b.y, s)
     _lib.moe_combine(b.y, b.topk_weights, T, k, H, b.out, s)
     return b.out

@@ -62,6 +62,7 @@ def device_inputs(inp, key=None):
         w2=bf16_tensor(inp.w2),
         bias=None if inp.router_bias is None else torch.from_numpy(inp.router_bias).cuda(),
     )
+    d["packed"] = moe.pack_experts(d["w13"], d["w2"])
     if key is not None:
         _device_cache.clear()  # keep one full-size set resident at a time
         _device_cache[key] = d
@@ -73,10 +74,26 @@ def run_layer(inp, dev=None, block_m=None, out_dtype=torch.bfloat16):
     s = inp.shape
     dev = dev or device_inputs(inp)
     bufs = moe.allocate(s.T, s.H, s.E, s.k, s.I, "cuda", block_m, out_dtype)
-    out = moe.moe_layer(dev["x"], dev["w_router"], dev["w13"], dev["w2"], top_k=s.k,
+    out = moe.moe_layer(dev["x"], dev["w_router"], top_k=s.k, packed=dev["packed"],
                         norm_topk_prob=s.norm_topk_prob, router_bias=dev["bias"], buffers=bufs)
     torch.cuda.synchronize()
     return out, bufs
+
+
+def pack_reference(w: np.ndarray, gated: bool) -> np.ndarray:
+    """The packed fragment layout built with numpy from its definition:
+    16-row bands x 32-column k-steps, block = 64 lanes x 8 values, lane l
+    holding row l%16 at columns 8*(l//16)..; gate/up bands interleaved."""
+    E, N, K = w.shape
+    if gated:
+        I = N // 2
+        g = w[:, :I].reshape(E, I // 16, 16, K)
+        u = w[:, I:].reshape(E, I // 16, 16, K)
+        bands = np.stack([g, u], axis=2).reshape(E, N // 16, 16, K)
+    else:
+        bands = w.reshape(E, N // 16, 16, K)
+    b = bands.reshape(E, N // 16, 16, K // 32, 4, 8)  # e, band, row, kstep, chunk, 8
+    return np.ascontiguousarray(b.transpose(0, 1, 3, 4, 2, 5)).reshape(E, N, K)
 
 
 def sample_tokens(T: int, n: int, seed: int = 0) -> np.ndarray:

@@ -100,6 +100,18 @@ def test_gemm_validation():
         assert fn(NULL, NULL, NULL, NULL, NULL, 0, 2, 64, 32, 8, 16, 0, NULL, NULL) == _lib.MOE_OK
 
 
+def test_pack_validation():
+    L = _raw()
+    assert moe.moe_packed_weight_bytes(128, 1536, 2048) == 128 * 1536 * 2048 * 2
+    assert moe.moe_packed_weight_bytes(2, 24, 64) == 0
+    other = ctypes.c_void_p(0x2000)
+    assert L.moe_pack_weights(FAKE, other, 2, 24, 64, 0, NULL) == _lib.MOE_ERR_UNSUPPORTED
+    assert L.moe_pack_weights(FAKE, other, 2, 32, 48, 0, NULL) == _lib.MOE_ERR_UNSUPPORTED
+    assert L.moe_pack_weights(FAKE, other, 2, 48, 64, 1, NULL) == _lib.MOE_ERR_UNSUPPORTED  # gated needs I % 16
+    assert L.moe_pack_weights(FAKE, FAKE, 2, 32, 64, 0, NULL) == _lib.MOE_ERR_INVALID  # in place
+    assert L.moe_pack_weights(NULL, other, 2, 32, 64, 0, NULL) == _lib.MOE_ERR_INVALID
+
+
 def test_combine_validation():
     L = _raw()
     assert L.moe_combine(FAKE, FAKE, 4, 2, 64, FAKE, 7, NULL) == _lib.MOE_ERR_INVALID
@@ -112,9 +124,9 @@ def test_combine_validation():
 def test_python_binding_rejects_host_tensors_and_wrong_dtypes():
     x = torch.zeros(4, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError, match="GPU"):
-        moe.moe_combine(torch.zeros(8, 64, dtype=torch.bfloat16), torch.zeros(4, 2), 4, 2, 64, x)
-    with pytest.raises(TypeError):
         moe.moe_combine(torch.zeros(8, 64), torch.zeros(4, 2), 4, 2, 64, x)
+    with pytest.raises(TypeError):
+        moe.moe_combine(torch.zeros(8, 64, dtype=torch.bfloat16), torch.zeros(4, 2), 4, 2, 64, x)
     with pytest.raises(ValueError, match="Unsupported activation"):
         moe.MoEConfig(64, 8, 2, 32, hidden_act="gelu")
 

@@ -14,7 +14,7 @@ import oracle
 import synth
 import sparse_mixture_experts_softmax_amd as moe
 from gpu_cases import (CONFIG_NAMES, bf16_tensor, custom_inputs, device_inputs, host_inputs, layer_tolerance, log,
-                       logits_bound, run_layer, sample_tokens, to_bits)
+                       logits_bound, pack_reference, run_layer, sample_tokens, to_bits)
 
 pytestmark = pytest.mark.gpu
 
@@ -134,6 +134,21 @@ def test_align_bitexact_edge_shapes(T, k, E, bm):
 
 
 # ----------------------------------------------------------------------------
+# Weight packing
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("E,N,K,gated", [(3, 64, 64, True), (2, 96, 160, False), (5, 1536, 2048, True),
+                                         (4, 2048, 768, False), (1, 32, 32, True)])
+def test_pack_weights_matches_layout_definition(E, N, K, gated):
+    bits = synth.normal_bf16(E * N + K, 99, (E, N, K), 1.0)
+    src = bf16_tensor(bits)
+    dst = torch.empty_like(src)
+    moe.moe_pack_weights(src, dst, E, N, K, gated)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_bits(dst), pack_reference(bits, gated))
+    assert np.array_equal(to_bits(src), bits)  # input untouched
+
+
+# ----------------------------------------------------------------------------
 # Each kernel against the oracle step it implements
 # ----------------------------------------------------------------------------
 @pytest.mark.parametrize("name", ["tiny", "decode", "prefill", "large"])
@@ -167,7 +182,8 @@ def test_gemms_and_combine_against_oracle_steps(name):
         y_ref.append(oracle.expert_down(a_gpu, inp.w2[e])[0])
         y_gpu.append(_f64(b.y[i]))
     elem_close(np.array(act_gpu), np.array(act_ref), what="gate_up act")
-    elem_close(np.array(y_gpu), np.array(y_ref), what="down y")
+    # y is fp32: only fp32 accumulation error (far below the floor)
+    elem_close(np.array(y_gpu), np.array(y_ref), rel=1e-5, floor_frac=1e-4, what="down y")
     # combine: fp32 output against the oracle's weighted sum of the GPU's y
     toks = sample_tokens(s.T, 128)
     out32 = torch.empty((s.T, s.H), dtype=torch.float32, device="cuda")
@@ -176,7 +192,7 @@ def test_gemms_and_combine_against_oracle_steps(name):
     y3 = _f64(b.y).reshape(s.T, s.k, s.H)[toks]
     w3 = b.topk_weights.cpu().numpy().astype(np.float64)[toks]
     ref = oracle.combine(y3, w3)
-    tol = (s.k + 1) * 2.0 ** -23 * (np.abs(w3)[:, :, None] * np.abs(y3)).sum(1) + 1e-30
+    tol = (s.k + 1) * 2.0 ** -23 * (np.abs(w3)[:, :, None] * np.abs(y3)).sum(1) + 1e-30  # fp32 sum of k products
     assert (np.abs(out32.cpu().numpy()[toks] - ref) <= tol).all()
     elem_close(_f64(out)[toks], ref, rel=2.0 ** -8, floor_frac=1e-6, what="combine bf16")
 
@@ -212,7 +228,7 @@ def test_layer_edge_cases():
         ("ragged", 37, 128, 8, 2, 96, True),
         ("dense", 45, 128, 1, 1, 64, True),
         ("k_eq_E", 20, 64, 8, 8, 32, False),
-        ("wide", 33, 64, 256, 32, 32, True),
+        ("wide", 33, 1024, 256, 32, 32, True),
         ("no_renorm", 50, 192, 12, 3, 160, False),
         ("multi_tile", 600, 64, 16, 8, 64, True),
     ]
@@ -231,7 +247,7 @@ def test_zero_tokens_is_a_noop():
     dev = device_inputs(inp)
     out = torch.full((0, 64), 3.0, dtype=torch.bfloat16, device="cuda")
     x0 = dev["x"][:0]
-    res = moe.moe_layer(x0, dev["w_router"], dev["w13"], dev["w2"], top_k=2)
+    res = moe.moe_layer(x0, dev["w_router"], top_k=2, packed=dev["packed"])
     torch.cuda.synchronize()
     assert res.shape == (0, 64) and out.shape == (0, 64)
 
@@ -251,14 +267,15 @@ def test_nan_poison_unused_experts_and_pad_rows():
     w2p[unused] = NAN_BF16
     dev = device_inputs(inp)
     dev = dict(dev, w13=bf16_tensor(w13p), w2=bf16_tensor(w2p))
+    dev["packed"] = moe.pack_experts(dev["w13"], dev["w2"])
     out, b = run_layer(inp, dev, block_m=32)
     assert np.array_equal(to_bits(out), to_bits(clean))
     # poison pad rows of act between the two GEMMs
     n = s.T * s.k
     pad = torch.from_numpy(np.nonzero(b.sorted_ids.cpu().numpy() == n)[0]).cuda()
     b.act[pad] = float("nan")
-    moe.moe_grouped_gemm_down(b.act, dev["w2"], b.sorted_ids, b.block_expert, b.num_padded, s.T, s.k, s.H, s.I, s.E,
-                              b.block_m, b.cap, b.y)
+    moe.moe_grouped_gemm_down(b.act, dev["packed"].w2, b.sorted_ids, b.block_expert, b.num_padded, s.T, s.k, s.H,
+                              s.I, s.E, b.block_m, b.cap, b.y)
     out2 = torch.empty_like(out)
     moe.moe_combine(b.y, b.topk_weights, s.T, s.k, s.H, out2)
     torch.cuda.synchronize()
@@ -314,6 +331,11 @@ def test_python_errors_on_gpu():
     inp = custom_inputs("err", 8, 64, 8, 2, 32)
     dev = device_inputs(inp)
     with pytest.raises(moe.MoEError, match="k="):
-        moe.moe_layer(dev["x"], dev["w_router"], dev["w13"], dev["w2"], top_k=9)
+        moe.moe_layer(dev["x"], dev["w_router"], top_k=9, packed=dev["packed"])
     with pytest.raises(ValueError, match="shape mismatch"):
         moe.moe_layer(dev["x"], dev["w_router"], dev["w2"], dev["w2"], top_k=2)
+    # row-major weights are packed on the fly and give the same result
+    a = moe.moe_layer(dev["x"], dev["w_router"], dev["w13"], dev["w2"], top_k=2)
+    b = moe.moe_layer(dev["x"], dev["w_router"], top_k=2, packed=dev["packed"])
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
