@@ -38,20 +38,23 @@ __global__ __launch_bounds__(kAlignThreads) void align_hist_kernel(const int32_t
     for (int e = threadIdx.x; e < E; e += blockDim.x) ws[(int64_t)blockIdx.x * E + e] = cnt[e];
 }
 
-// Inclusive scan of v over the workgroup's first E threads' values (E <= 256),
-// Hillis-Steele in LDS. Returns the inclusive prefix for thread tid < E.
-__device__ int block_inclusive_scan(int v, int* buf, int E) {
-    const int tid = threadIdx.x;
-    if (tid < kMaxExperts) buf[tid] = tid < E ? v : 0;
-    __syncthreads();
-    for (int d = 1; d < kMaxExperts; d <<= 1) {
-        int add = 0;
-        if (tid < kMaxExperts && tid >= d) add = buf[tid - d];
-        __syncthreads();
-        if (tid < kMaxExperts) buf[tid] += add;
-        __syncthreads();
+// Inclusive scan over the workgroup's first kMaxExperts threads (values of
+// threads >= E count as 0): a shuffle scan inside each wave, then the wave
+// totals. Every thread of the workgroup must call it.
+__device__ int block_inclusive_scan(int v, int* wave_tot, int E) {
+    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    int x = tid < E ? v : 0;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        const int y = __shfl_up(x, d, kWave);
+        if (lane >= d) x += y;
     }
-    return tid < kMaxExperts ? buf[tid] : 0;
+    if (lane == kWave - 1) wave_tot[wave] = x;
+    __syncthreads();
+    int add = 0;
+    for (int w = 0; w < wave; ++w) add += wave_tot[w];
+    __syncthreads();
+    return x + add;
 }
 
 __global__ __launch_bounds__(kAlignThreads) void align_scatter_kernel(
@@ -61,7 +64,7 @@ __global__ __launch_bounds__(kAlignThreads) void align_scatter_kernel(
     __shared__ int total[kMaxExperts];    // c_e
     __shared__ int base[kMaxExperts];     // next position of this tile's pairs of expert e (relative to off)
     __shared__ int off[kMaxExperts + 1];  // padded exclusive scan; off[E] = num_padded
-    __shared__ int scan_buf[kMaxExperts];
+    __shared__ int scan_buf[kAlignWaves];
     __shared__ int wcnt[kAlignWaves][kMaxExperts];
     const int tid = threadIdx.x;
     const int lane = tid % kWave, wave = tid / kWave;
@@ -102,24 +105,22 @@ __global__ __launch_bounds__(kAlignThreads) void align_scatter_kernel(
         if (tid == 0) *num_padded = npad;
     }
 
-    // Pad rows and block owners for this workgroup's share of [0, cap).
-    const int64_t nblocks = cap / BM;
-    const int64_t blocks_per = (nblocks + ntiles - 1) / ntiles;
-    const int64_t b_lo = (int64_t)tile * blocks_per, b_hi = min(nblocks, b_lo + blocks_per);
-    for (int64_t r = b_lo * BM + tid; r < b_hi * BM; r += blockDim.x) {
-        if (r >= npad) {
+    // Pad rows (sentinel) and block owners. Expert e's share is done by
+    // workgroup e % ntiles (thread e / ntiles); rows from num_padded to cap
+    // are split over all workgroups.
+    for (int e = tile + (int)(tid * ntiles); e < E; e += (int)(blockDim.x * ntiles)) {
+        const int o = off[e], c = total[e], p = off[e + 1] - o;
+        for (int r = o + c; r < o + p; ++r) sorted_ids[r] = (int32_t)n;
+        for (int b = o / BM; b < (o + p) / BM; ++b) block_expert[b] = e;
+    }
+    {
+        const int64_t rest = cap - npad;
+        const int64_t per = (rest + ntiles - 1) / ntiles;
+        const int64_t lo = npad + (int64_t)tile * per, hi = min(cap, lo + per);
+        for (int64_t r = lo + tid; r < hi; r += blockDim.x) {
             sorted_ids[r] = (int32_t)n;
             if (r % BM == 0) block_expert[r / BM] = -1;
-            continue;
         }
-        int lo = 0, hi = E - 1;  // largest e with off[e] <= r
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) / 2;
-            if (off[mid] <= r) lo = mid;
-            else hi = mid - 1;
-        }
-        if (r - off[lo] >= total[lo]) sorted_ids[r] = (int32_t)n;
-        if (r % BM == 0) block_expert[r / BM] = lo;
     }
 
     // Stable scatter of this tile's pairs.
