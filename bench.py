@@ -275,7 +275,9 @@ def main():
         achieved = work[dom]["flops"] / dom_s / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4)}
-    roof["kernel"] = "grouped_gemm_kernel<gate_up> (moe_grouped_gemm_gate_up_silu)"
+    roof["kernel"] = ("moe_grouped_gemm_gate_up_silu: " +
+                      ("grouped_gemm_skinny_kernel<true,...>" if block_m == 16 else
+                       f"grouped_gemm_kernel<GemmCfg<{block_m},128,true>>"))
     roof["kernel_ms"] = round(dom_ms, 5)
     roof["timing"] = (f"HIP events around each of the {args.steps} launches in a second timed region of "
                       f"{args.steps} steps ({elapsed_marked * 1e3 / args.steps:.4f} ms/step with the markers)")
