@@ -215,10 +215,13 @@ int moe_grouped_gemm_down(const void* act, const void* w2, const int32_t* sorted
 int moe_combine(const void* y, const float* topk_weights, int64_t T, int32_t k, int32_t H, void* out,
                 int32_t out_dtype, void* stream);
 
-/* The block_m the library's GEMMs run fastest with for this routing shape
- * (a tile-size choice only; every valid block_m gives the same result up to
- * fp32 rounding of the accumulation order, which does not depend on
- * block_m). Returns -1 on invalid arguments. */
+/* The block_m the library's GEMMs run fastest with for this routing shape.
+ * A tile-size choice only: for a fixed block_m every result is bit-for-bit
+ * reproducible and independent of the other tokens in the batch; different
+ * block_m values use different matrix-core instruction shapes (16x16x32 for
+ * 16 and 32, 32x32x16 for 64 and 128), whose fp32 accumulation orders differ,
+ * so their outputs agree to rounding, not bit for bit. Returns -1 on invalid
+ * arguments. */
 int32_t moe_pick_block_m(int64_t T, int32_t k, int32_t E);
 
 #ifdef __cplusplus

@@ -221,6 +221,223 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(
     }
 }
 
+// Wide variant for row blocks of 64 or 128 (tens to thousands of rows per
+// expert, as in prefill): matrix-core bound, so it runs on
+// v_mfma_f32_32x32x16_bf16 (on gfx950 the 16x16x32 form issues at about half
+// the rate) with 64x128 wave tiles (2x4 accumulator tiles of 32x32, 128
+// accumulator registers); the workgroup covers BM rows x 512 weight rows
+// with (BM/64) x 4 waves.
+//
+// Operands reach LDS by direct global->LDS copies (global_load_lds_dwordx4,
+// no registers), S stages deep: stage kt holds the activation rows' columns
+// [32kt, 32kt+32) and one packed 1 KB block per weight band. The A rows are
+// stored 64 bytes apart with their four 16-byte chunks XOR-swizzled by
+// (row/4)%4 so that fragment reads are free of bank conflicts; B blocks are
+// stored as packed. Each wave waits only for its own copies of the stage it
+// needs (explicit vmcnt), then a bare s_barrier publishes the stage to all
+// waves and frees the oldest one for the next copy.
+//
+// Tiles are ordered so each XCD (workgroups go to the 8 XCDs round robin)
+// takes a contiguous share of the real (row block, N tile) pairs, N-tile
+// major and row block minor: the row blocks of one expert run together on one
+// XCD and share its L2 for the weight tile.
+template <bool GATED_, int BM_, int STAGES_>
+struct WideCfg {
+    static constexpr bool GATED = GATED_;
+    static constexpr int BM = BM_;
+    static constexpr int WAVES_M = BM / 64;
+    static constexpr int WAVES_N = 4;
+    static constexpr int THREADS = WAVES_M * WAVES_N * kWave;
+    static constexpr int WTN = 128;              // weight rows per wave
+    static constexpr int BN = WAVES_N * WTN;     // weight rows per workgroup
+    static constexpr int COLS = GATED ? BN / 2 : BN;  // output columns per workgroup
+    static constexpr int TM = 2, TN = 4;         // 32x32 accumulator tiles per wave
+    static constexpr int STAGES = STAGES_;
+    static constexpr int A_BYTES = BM * 64;      // one stage of A: BM rows x 32 columns
+    static constexpr int B_BYTES = BN * 64;      // BN/16 packed blocks of 1 KB
+    static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
+    static constexpr int COPIES = (BM + BN) / 16;  // 1 KB copies per stage
+    static constexpr int COPIES_PER_WAVE = COPIES / (WAVES_M * WAVES_N);
+    static_assert(COPIES % (WAVES_M * WAVES_N) == 0, "copies must split evenly over the waves");
+    static_assert(STAGES >= 2 && STAGES <= 5, "stages");
+    static_assert(STAGES * STAGE_BYTES + BM * 8 <= 160 * 1024, "LDS");
+};
+
+template <class C>
+__global__ __launch_bounds__(C::THREADS) void grouped_gemm_wide_kernel(
+    const uint16_t* __restrict__ a_src, const uint16_t* __restrict__ w, const int32_t* __restrict__ sorted_ids,
+    const int32_t* __restrict__ block_expert, const int32_t* __restrict__ num_padded, int k, int64_t n_pairs,
+    int K, int N_out, int n_tiles, void* __restrict__ out) {
+    constexpr int BM = C::BM, S = C::STAGES;
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    __shared__ int64_t row_src[BM];  // gate/up: x row offset (-1 = sentinel); down: y row (-1 = skip)
+
+    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    // XCD-aware tile order over the real tiles only
+    const int m_real = *num_padded / BM;
+    const int64_t real = (int64_t)m_real * n_tiles;
+    const int64_t share = (real + 7) / 8;
+    const int64_t logical = (int64_t)(blockIdx.x % 8) * share + blockIdx.x / 8;
+    if ((int64_t)(blockIdx.x / 8) >= share || logical >= real) return;
+    const int tn = (int)(logical / m_real), mb = (int)(logical % m_real);
+    const int e = block_expert[mb];
+    if (e < 0) return;
+    const int64_t w_rows = C::GATED ? 2 * (int64_t)N_out : (int64_t)N_out;
+    const int bands = (int)(w_rows / 16);
+    const uint16_t* we = w + (int64_t)e * w_rows * K;
+
+    for (int i = tid; i < BM; i += C::THREADS) {
+        const int32_t id = sorted_ids[(int64_t)mb * BM + i];
+        const bool ok = id >= 0 && (int64_t)id < n_pairs;
+        if (C::GATED) row_src[i] = ok ? (int64_t)(id / k) * K : -1;
+        else row_src[i] = ok ? (int64_t)id : -1;
+    }
+    __syncthreads();
+
+    // This wave's copies: index q over [A rows 16q.. | B band q - BM/16].
+    const uint16_t* src[C::COPIES_PER_WAVE];
+    int dst[C::COPIES_PER_WAVE];  // byte offset inside a stage (wave-uniform)
+#pragma unroll
+    for (int j = 0; j < C::COPIES_PER_WAVE; ++j) {
+        const int q = wave * C::COPIES_PER_WAVE + j;
+        if (q < BM / 16) {
+            const int row = q * 16 + lane / 4;
+            const int chunk = (lane % 4) ^ ((row >> 2) & 3);  // LDS slot lane%4 holds this chunk
+            int64_t base;
+            if (C::GATED) base = row_src[row] >= 0 ? row_src[row] : 0;  // sentinel rows: any valid row
+            else base = ((int64_t)mb * BM + row) * K;
+            src[j] = a_src + base + chunk * 8;
+            dst[j] = q * 1024;
+        } else {
+            const int bt = q - BM / 16;
+            const int band = min(tn * (C::BN / 16) + bt, bands - 1);
+            src[j] = we + (int64_t)band * 16 * K + lane * 8;
+            dst[j] = C::A_BYTES + bt * 1024;
+        }
+    }
+    const int nkt = K / 32;
+    auto issue = [&](int kt) {
+        char* stage = smem + (kt % S) * C::STAGE_BYTES;
+#pragma unroll
+        for (int j = 0; j < C::COPIES_PER_WAVE; ++j) {
+            const int q = wave * C::COPIES_PER_WAVE + j;
+            const int64_t step = q < BM / 16 ? 32 : 512;  // A: 32 columns; B: one packed block
+            lds_dma16(src[j] + kt * step, stage + dst[j]);
+        }
+    };
+
+    const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
+    // B band pairs (32 weight rows) of each accumulator column tile
+    int band_lo[C::TN], band_hi[C::TN];
+#pragma unroll
+    for (int t = 0; t < C::TN; ++t) {
+        if (C::GATED) {
+            const int g = t % (C::TN / 2);
+            const int cb = wn * (C::WTN / 32) + g * 2;  // output column block (16 wide) within the tile
+            const int up = t < C::TN / 2 ? 0 : 1;
+            band_lo[t] = 2 * cb + up;
+            band_hi[t] = 2 * (cb + 1) + up;
+        } else {
+            band_lo[t] = wn * (C::WTN / 16) + 2 * t;
+            band_hi[t] = band_lo[t] + 1;
+        }
+    }
+    f32x16 acc[C::TM][C::TN];
+#pragma unroll
+    for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+        for (int t = 0; t < C::TN; ++t) acc[i][t] = f32x16{};
+
+#pragma unroll
+    for (int p = 0; p < S - 1; ++p)
+        if (p < nkt) issue(p);
+    for (int kt = 0; kt < nkt; ++kt) {
+        // wait for this wave's copies of stage kt (the copies of up to S-2
+        // later stages may still be in flight), then publish it
+        const int later = min(S - 2, nkt - 1 - kt);
+        if (later >= 3) vm_wait<3 * C::COPIES_PER_WAVE>();
+        else if (later == 2) vm_wait<2 * C::COPIES_PER_WAVE>();
+        else if (later == 1) vm_wait<C::COPIES_PER_WAVE>();
+        else vm_wait<0>();
+        __builtin_amdgcn_s_barrier();
+        if (kt + S - 1 < nkt) issue(kt + S - 1);
+        const char* stage = smem + (kt % S) * C::STAGE_BYTES;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            u32x4 fa[C::TM], fb[C::TN];
+            const int chunk = 2 * ks + lane / 32;
+#pragma unroll
+            for (int i = 0; i < C::TM; ++i) {
+                const int r = wm * 64 + i * 32 + lane % 32;
+                fa[i] = *(const u32x4*)(stage + r * 64 + ((chunk ^ ((r >> 2) & 3)) * 16));
+            }
+#pragma unroll
+            for (int t = 0; t < C::TN; ++t) {
+                const int band = (lane % 32) < 16 ? band_lo[t] : band_hi[t];
+                fb[t] = *(const u32x4*)(stage + C::A_BYTES + band * 1024 + (chunk * 16 + lane % 16) * 16);
+            }
+#pragma unroll
+            for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+                for (int t = 0; t < C::TN; ++t) acc[i][t] = mfma32x32x16(fa[i], fb[t], acc[i][t]);
+        }
+    }
+
+    // Epilogue: element q of a 32x32 tile is row 8*(q/4) + 4*(lane/32) + q%4,
+    // column lane%32.
+    if (C::GATED) {
+#pragma unroll
+        for (int g = 0; g < C::TN / 2; ++g) {
+            const int col = tn * C::COLS + wn * (C::WTN / 2) + g * 32 + lane % 32;
+            if (col >= N_out) continue;
+#pragma unroll
+            for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+                for (int q = 0; q < 16; ++q) {
+                    const int row = wm * 64 + i * 32 + 8 * (q / 4) + 4 * (lane / 32) + q % 4;
+                    const float v = row_src[row] >= 0 ? silu(acc[i][g][q]) * acc[i][g + C::TN / 2][q] : 0.f;
+                    ((uint16_t*)out)[((int64_t)mb * BM + row) * N_out + col] = f32_to_bf16(v);
+                }
+        }
+    } else {
+#pragma unroll
+        for (int t = 0; t < C::TN; ++t) {
+            const int col = tn * C::COLS + wn * C::WTN + t * 32 + lane % 32;
+            if (col >= N_out) continue;
+#pragma unroll
+            for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+                for (int q = 0; q < 16; ++q) {
+                    const int row = wm * 64 + i * 32 + 8 * (q / 4) + 4 * (lane / 32) + q % 4;
+                    const int64_t dst_row = row_src[row];
+                    if (dst_row >= 0) ((float*)out)[dst_row * N_out + col] = acc[i][t][q];
+                }
+        }
+    }
+}
+
+template <class C>
+static int launch_wide(const void* a, const void* w, const int32_t* sorted_ids, const int32_t* block_expert,
+                       const int32_t* num_padded, int k, int64_t n_pairs, int K, int N_out, int64_t cap, void* out,
+                       hipStream_t s, const char* what) {
+    const int n_tiles = (N_out + C::COLS - 1) / C::COLS;
+    int64_t grid = (cap / C::BM) * n_tiles;
+    grid = (grid + 7) / 8 * 8;
+    if (grid >= ((int64_t)1 << 31)) return set_error(MOE_ERR_UNSUPPORTED, "%s: grid too large", what);
+    const size_t lds = (size_t)C::STAGES * C::STAGE_BYTES;
+    static bool attr_set = false;  // the dynamic LDS size exceeds the 64 KB default
+    if (!attr_set) {
+        hipError_t err = hipFuncSetAttribute((const void*)grouped_gemm_wide_kernel<C>,
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (err != hipSuccess) return set_error(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(err));
+        attr_set = true;
+    }
+    hipLaunchKernelGGL(grouped_gemm_wide_kernel<C>, dim3((unsigned)grid), dim3(C::THREADS), lds, s,
+                       (const uint16_t*)a, (const uint16_t*)w, sorted_ids, block_expert, num_padded, k, n_pairs, K,
+                       N_out, n_tiles, out);
+    return check_launch(what);
+}
+
 // Skinny variant for 16-row blocks (a handful of rows per expert, as in
 // decode): the work is streaming each touched expert's weights once, so the
 // weights bypass LDS. Each wave owns NTILE packed 16-row bands (gate/up:
@@ -386,11 +603,11 @@ static int dispatch_gemm(int32_t block_m, const void* a, const void* w, const in
             return launch_gemm<GemmCfg<32, 128, GATED>>(a, w, sorted_ids, block_expert, num_padded, k, n_pairs, K,
                                                        N_out, cap, out, s, what);
         case 64:
-            return launch_gemm<GemmCfg<64, 128, GATED>>(a, w, sorted_ids, block_expert, num_padded, k, n_pairs, K,
-                                                       N_out, cap, out, s, what);
+            return launch_wide<WideCfg<GATED, 64, 4>>(a, w, sorted_ids, block_expert, num_padded, k, n_pairs, K,
+                                                      N_out, cap, out, s, what);
         case 128:
-            return launch_gemm<GemmCfg<128, 128, GATED>>(a, w, sorted_ids, block_expert, num_padded, k, n_pairs, K,
-                                                        N_out, cap, out, s, what);
+            return launch_wide<WideCfg<GATED, 128, 3>>(a, w, sorted_ids, block_expert, num_padded, k, n_pairs, K,
+                                                       N_out, cap, out, s, what);
     }
     return set_error(MOE_ERR_UNSUPPORTED, "%s: block_m=%d not in {16,32,64,128}", what, block_m);
 }
@@ -444,9 +661,12 @@ extern "C" int moe_grouped_gemm_down(const void* act, const void* w2, const int3
 
 extern "C" int32_t moe_pick_block_m(int64_t T, int32_t k, int32_t E) {
     if (T < 0 || k < 1 || E < 1) return -1;
+    // 16: weight streaming (skinny kernel); 32: few rows per expert; 128: the
+    // matrix-core bound regime, where the 8-wave 128x512 tile (two waves per
+    // SIMD) beats 64-row blocks despite the extra padding (measured on the
+    // prefill, skewed and large workloads).
     const double rows_per_expert = (double)T * k / E;
     if (rows_per_expert <= 24) return 16;
-    if (rows_per_expert <= 96) return 32;
-    if (rows_per_expert <= 384) return 64;
+    if (rows_per_expert <= 64) return 32;
     return 128;
 }

@@ -45,6 +45,31 @@ __device__ __forceinline__ u32x4 sel(bool keep, u32x4 v) {
     return u32x4{keep ? v[0] : 0u, keep ? v[1] : 0u, keep ? v[2] : 0u, keep ? v[3] : 0u};
 }
 
+// D(32x32, fp32) += A(32x16, bf16) * B(16x32, bf16). Lane l supplies row
+// l%32 of A and column l%32 of B, eight k each at k-offset 8*(l/32); it
+// receives D[8*(i/4) + 4*(l/32) + i%4][l%32] in element i (checked on the
+// device).
+__device__ __forceinline__ f32x16 mfma32x32x16(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Direct global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4):
+// lane l's 16 bytes land at lds_base + 16*l. lds_base must be wave-uniform.
+// The compiler does not order later LDS reads after these copies: callers
+// wait with vm_wait() and a barrier.
+__device__ __forceinline__ void lds_dma16(const void* g, void* lds_base) {
+    __builtin_amdgcn_global_load_lds(g, (lds_void*)lds_base, 16, 0, 0);
+}
+
+// s_waitcnt vmcnt(N) (gfx9 encoding; expcnt and lgkmcnt left unconstrained).
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
 
 template <typename T>

@@ -320,11 +320,19 @@ def test_expert_relabelling_bit_identical():
     assert np.array_equal(to_bits(out_p), to_bits(out))
 
 
-def test_block_m_does_not_change_results():
+def test_block_m_changes_results_only_by_rounding():
+    """16/32 and 64/128 share an MFMA shape: bit-identical within each pair;
+    across shapes the fp32 accumulation order differs, so outputs agree to
+    bf16 rounding and each matches the oracle."""
     inp = custom_inputs("tiles", 900, 512, 16, 4, 256, seed=9)
-    outs = [to_bits(run_layer(inp, block_m=bm)[0]) for bm in (16, 32, 64, 128)]
-    for o in outs[1:]:
-        assert np.array_equal(o, outs[0])
+    outs = {bm: run_layer(inp, block_m=bm)[0] for bm in (16, 32, 64, 128)}
+    assert np.array_equal(to_bits(outs[16]), to_bits(outs[32]))
+    assert np.array_equal(to_bits(outs[64]), to_bits(outs[128]))
+    a, b = _f64(outs[16]), _f64(outs[64])
+    assert (np.abs(a - b) <= 2.0 ** -7 * np.abs(a) + 1e-3 * np.sqrt(np.mean(a ** 2))).all()
+    ref, _, _ = oracle.moe_layer(inp.x, inp.w_router, inp.w13, inp.w2, 4, True)
+    for bm, o in outs.items():
+        assert np.abs(_f64(o) - ref).max() <= layer_tolerance(ref), bm
 
 
 def test_python_errors_on_gpu():
