@@ -241,9 +241,10 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(
 // takes a contiguous share of the real (row block, N tile) pairs, N-tile
 // major and row block minor: the row blocks of one expert run together on one
 // XCD and share its L2 for the weight tile.
-template <bool GATED_, int BM_, int STAGES_>
+template <bool GATED_, int BM_, int STAGES_, bool MB_MAJOR_ = true>
 struct WideCfg {
     static constexpr bool GATED = GATED_;
+    static constexpr bool MB_MAJOR = MB_MAJOR_;  // tile order inside an XCD's share
     static constexpr int BM = BM_;
     static constexpr int WAVES_M = BM / 64;
     static constexpr int WAVES_N = 4;
@@ -260,7 +261,7 @@ struct WideCfg {
     static constexpr int COPIES_PER_WAVE = COPIES / (WAVES_M * WAVES_N);
     static_assert(COPIES % (WAVES_M * WAVES_N) == 0, "copies must split evenly over the waves");
     static_assert(STAGES >= 2 && STAGES <= 5, "stages");
-    static_assert(STAGES * STAGE_BYTES + BM * 8 <= 160 * 1024, "LDS");
+    static_assert(STAGES * STAGE_BYTES <= 160 * 1024, "LDS");
 };
 
 template <class C>
@@ -270,7 +271,6 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_wide_kernel(
     int K, int N_out, int n_tiles, void* __restrict__ out) {
     constexpr int BM = C::BM, S = C::STAGES;
     extern __shared__ __attribute__((aligned(16))) char smem[];
-    __shared__ int64_t row_src[BM];  // gate/up: x row offset (-1 = sentinel); down: y row (-1 = skip)
 
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
     // XCD-aware tile order over the real tiles only
@@ -279,20 +279,16 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_wide_kernel(
     const int64_t share = (real + 7) / 8;
     const int64_t logical = (int64_t)(blockIdx.x % 8) * share + blockIdx.x / 8;
     if ((int64_t)(blockIdx.x / 8) >= share || logical >= real) return;
-    const int tn = (int)(logical / m_real), mb = (int)(logical % m_real);
+    const int tn = C::MB_MAJOR ? (int)(logical % n_tiles) : (int)(logical / m_real);
+    const int mb = C::MB_MAJOR ? (int)(logical / n_tiles) : (int)(logical % m_real);
     const int e = block_expert[mb];
     if (e < 0) return;
     const int64_t w_rows = C::GATED ? 2 * (int64_t)N_out : (int64_t)N_out;
     const int bands = (int)(w_rows / 16);
     const uint16_t* we = w + (int64_t)e * w_rows * K;
 
-    for (int i = tid; i < BM; i += C::THREADS) {
-        const int32_t id = sorted_ids[(int64_t)mb * BM + i];
-        const bool ok = id >= 0 && (int64_t)id < n_pairs;
-        if (C::GATED) row_src[i] = ok ? (int64_t)(id / k) * K : -1;
-        else row_src[i] = ok ? (int64_t)id : -1;
-    }
-    __syncthreads();
+    const int32_t* ids_blk = sorted_ids + (int64_t)mb * BM;
+    auto real_row = [&](int32_t id) { return id >= 0 && (int64_t)id < n_pairs; };
 
     // This wave's copies: index q over [A rows 16q.. | B band q - BM/16].
     const uint16_t* src[C::COPIES_PER_WAVE];
@@ -304,8 +300,12 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_wide_kernel(
             const int row = q * 16 + lane / 4;
             const int chunk = (lane % 4) ^ ((row >> 2) & 3);  // LDS slot lane%4 holds this chunk
             int64_t base;
-            if (C::GATED) base = row_src[row] >= 0 ? row_src[row] : 0;  // sentinel rows: any valid row
-            else base = ((int64_t)mb * BM + row) * K;
+            if (C::GATED) {
+                const int32_t id = ids_blk[row];
+                base = real_row(id) ? (int64_t)(id / k) * K : 0;  // sentinel rows: any valid row
+            } else {
+                base = ((int64_t)mb * BM + row) * K;
+            }
             src[j] = a_src + base + chunk * 8;
             dst[j] = q * 1024;
         } else {
@@ -395,7 +395,7 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_wide_kernel(
 #pragma unroll
                 for (int q = 0; q < 16; ++q) {
                     const int row = wm * 64 + i * 32 + 8 * (q / 4) + 4 * (lane / 32) + q % 4;
-                    const float v = row_src[row] >= 0 ? silu(acc[i][g][q]) * acc[i][g + C::TN / 2][q] : 0.f;
+                    const float v = real_row(ids_blk[row]) ? silu(acc[i][g][q]) * acc[i][g + C::TN / 2][q] : 0.f;
                     ((uint16_t*)out)[((int64_t)mb * BM + row) * N_out + col] = f32_to_bf16(v);
                 }
         }
@@ -409,8 +409,8 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_wide_kernel(
 #pragma unroll
                 for (int q = 0; q < 16; ++q) {
                     const int row = wm * 64 + i * 32 + 8 * (q / 4) + 4 * (lane / 32) + q % 4;
-                    const int64_t dst_row = row_src[row];
-                    if (dst_row >= 0) ((float*)out)[dst_row * N_out + col] = acc[i][t][q];
+                    const int32_t id = ids_blk[row];
+                    if (real_row(id)) ((float*)out)[(int64_t)id * N_out + col] = acc[i][t][q];
                 }
         }
     }
