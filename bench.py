@@ -41,7 +41,10 @@ WORKLOAD_TEXT = {
     "prefill": "prefill-shaped Qwen3-MoE layer",
     "skewed": "skewed-routing (Zipf 1.2) MoE layer",
     "large": "large MoE layer on one GPU",
+    "dense": "dense SwiGLU GatedMLP (Qwen3-0.6B MLP shape) through the grouped GEMMs",
+    "add_rmsnorm": "fused residual add + RMSNorm before the layer (prefill-shaped hidden state)",
 }
+NORM_SHAPE = (4096, 2048)  # tokens, hidden (the prefill-shaped layer's input)
 KERNELS = ["route", "align", "gate_up", "down", "combine"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = {
@@ -136,6 +139,75 @@ def cpu_baseline(inp, seconds: float):
     }
 
 
+def norm_bench(args):
+    """The fused residual add + RMSNorm that precedes the layer, in place on a
+    [4096, 2048] bf16 hidden state: HBM-bound (reads x and the residual,
+    writes both)."""
+    import numpy as np
+    import torch
+
+    import synth
+    import sparse_mixture_experts_softmax_amd as moe
+
+    T, H = NORM_SHAPE
+    progress(f"add_rmsnorm T={T} H={H}")
+    xb = synth.normal_bf16(args.seed, synth.TAG_X, (T, H), 1.0)
+    rb = synth.normal_bf16(args.seed, 0x200, (T, H), 1.0)
+    wb = synth.normal_bf16(args.seed, 0x201, (H,), 1.0)
+    dev = lambda a: torch.from_numpy(a).view(torch.bfloat16).cuda()  # noqa: E731
+    x, r, w = dev(xb), dev(rb), dev(wb)
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+
+    def step():
+        moe.moe_fused_add_rmsnorm(x, r, w, T, H, 1e-6, True, sp)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for a, b in evs:
+        a.record(stream)
+        step()
+        b.record(stream)
+    torch.cuda.synchronize()
+    kern_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    nbytes = 4 * T * H * 2 + H * 2
+    ms = elapsed * 1e3 / args.steps
+    achieved = nbytes / (kern_ms * 1e-3) / 1e9
+    result = {
+        "metric": "fused residual add + RMSNorm tokens/s; achieved HBM GB/s",
+        "value": round(T / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded N(0,1) hidden state and residual)",
+        "config": {"workload": WORKLOAD_TEXT["add_rmsnorm"], "T": T, "hidden": H, "eps": 1e-6},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBPS, 4), "kernel": "fused_add_rmsnorm_kernel<1>",
+                     "kernel_ms": round(kern_ms, 5), "algorithmic_per_launch": nbytes, "traffic": None},
+    }
+    if args.cpu_seconds > 0:
+        import oracle
+
+        n = 256
+        t1 = time.perf_counter()
+        reps = 0
+        while time.perf_counter() - t1 < min(args.cpu_seconds, 5.0):
+            oracle.fused_add_rmsnorm(xb[:n], rb[:n], wb, 1e-6)
+            reps += 1
+        dt = time.perf_counter() - t1
+        result["cpu_baseline"] = {"value": round(n * reps / dt, 1), "unit": "tokens/s",
+                                  "cores": oracle.default().max_threads(), "kind": "oracle",
+                                  "sample": f"first {n} rows x {reps} repeats, {dt:.1f} s"}
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
 def copy_calibration(mb: int):
     """A plain device-to-device copy of `mb` MiB, for scaling HBM counters."""
     import torch
@@ -180,6 +252,9 @@ def main():
     if args.copy_calibration_mb:
         copy_calibration(args.copy_calibration_mb)
         return
+    if args.workload == "add_rmsnorm":
+        norm_bench(args)
+        return
 
     shape = synth.CONFIGS[args.workload]
     progress(f"generating {args.workload} inputs (T={shape.T} H={shape.H} E={shape.E} k={shape.k} I={shape.I})")
@@ -205,16 +280,20 @@ def main():
     stream = torch.cuda.current_stream()
     sp = stream.cuda_stream
 
+    dense = args.workload == "dense"
+    if dense:
+        ids0 = torch.zeros((T, 1), dtype=torch.int32, device="cuda")
+        ones = torch.ones((T, 1), dtype=torch.float32, device="cuda")
     calls = [
-        lambda w13, w2: moe.moe_route(x, wr, bias, b.logits, b.topk_ids, b.topk_weights, T, H, E, k,
+        lambda w13, w2: None if dense else moe.moe_route(x, wr, bias, b.logits, b.topk_ids, b.topk_weights, T, H, E, k,
                                       shape.norm_topk_prob, sp),
-        lambda w13, w2: moe.moe_align_by_expert(b.topk_ids, T, k, E, block_m, b.sorted_ids, b.block_expert,
-                                                b.expert_counts, b.num_padded, b.workspace, sp),
+        lambda w13, w2: moe.moe_align_by_expert(ids0 if dense else b.topk_ids, T, k, E, block_m, b.sorted_ids,
+                                                b.block_expert, b.expert_counts, b.num_padded, b.workspace, sp),
         lambda w13, w2: moe.moe_grouped_gemm_gate_up_silu(x, w13, b.sorted_ids, b.block_expert, b.num_padded, T, k,
                                                           H, I, E, block_m, b.cap, b.act, sp),
         lambda w13, w2: moe.moe_grouped_gemm_down(b.act, w2, b.sorted_ids, b.block_expert, b.num_padded, T, k, H, I,
                                                   E, block_m, b.cap, b.y, sp),
-        lambda w13, w2: moe.moe_combine(b.y, b.topk_weights, T, k, H, b.out, sp),
+        lambda w13, w2: moe.moe_combine(b.y, ones if dense else b.topk_weights, T, k, H, b.out, sp),
     ]
     dom_idx = KERNELS.index("gate_up")
 
@@ -265,6 +344,8 @@ def main():
     work = algorithmic_work(shape, counts)
 
     bound = "hbm" if args.workload in ("decode", "tiny") else "mfma"
+    if dense:
+        work["layer"]["flops"] -= 2 * T * H * E  # no router
     dom = "gate_up"
     dom_s = dom_ms * 1e-3
     if bound == "hbm":

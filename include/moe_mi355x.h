@@ -215,6 +215,28 @@ int moe_grouped_gemm_down(const void* act, const void* w2, const int32_t* sorted
 int moe_combine(const void* y, const float* topk_weights, int64_t T, int32_t k, int32_t H, void* out,
                 int32_t out_dtype, void* stream);
 
+/*
+ * Fused residual add + RMSNorm, the step that precedes the MoE layer in a
+ * decoder layer (handbook page "The op layer: BaseOP and the layers",
+ * section "Ops: reference implementations and dispatch" for rmsnorm and
+ * fused_add_rmsnorm, section "RMSNorm and the residual" for the fused op and
+ * the first-layer case). In place, on [T, H] bf16 rows:
+ *   has_residual != 0:  residual <- bf16(residual + x)   (fp32 add)
+ *   has_residual == 0:  residual <- x                   (first layer)
+ *   x <- bf16(weight * bf16(residual / sqrt(mean(residual^2) + eps)))
+ * (the norm in fp32; the normalized value is cast to bf16 before the
+ * weight multiply, as the reference op does). The normalized x is the
+ * layer's input; residual carries the new residual stream.
+ *
+ *   x         [T, H] bf16, device, in/out.
+ *   residual  [T, H] bf16, device, in/out (input ignored when has_residual
+ *             is 0); must not alias x.
+ *   weight    [H] bf16, device.
+ * Limits: H a multiple of 8, at most 16384; eps >= 0. T == 0 is a no-op.
+ */
+int moe_fused_add_rmsnorm(void* x, void* residual, const void* weight, int64_t T, int32_t H, float eps,
+                          int32_t has_residual, void* stream);
+
 /* The block_m the library's GEMMs run fastest with for this routing shape.
  * A tile-size choice only: for a fixed block_m every result is bit-for-bit
  * reproducible and independent of the other tokens in the batch; different

@@ -17,6 +17,8 @@ function follows the passage cited in the C source:
 * ``expert_gate_up``, ``expert_down``, ``expert_mlp`` -- one expert's gated
   MLP and its two halves (GatedMLP on the "Models and weight loading" page).
 * ``combine``         -- the weighted sum of a token's k expert outputs.
+* ``fused_add_rmsnorm`` -- the residual add + RMSNorm that precedes the MLP
+  ("The op layer" page: reference ops and "RMSNorm and the residual").
 * ``moe_layer``       -- the whole layer, one token at a time.
 
 All of these are pinned by the tests in ``tests/test_oracle_*.py`` (brute
@@ -60,6 +62,8 @@ class OracleLib:
         lib.oracle_combine.restype = None
         lib.oracle_moe_layer.argtypes = [p, p, p, p, p, i64, i64, i64, i64, i64, ci, p, i64, p, p, p]
         lib.oracle_moe_layer.restype = None
+        lib.oracle_fused_add_rmsnorm.argtypes = [p, p, p, i64, i64, ctypes.c_double, ci]
+        lib.oracle_fused_add_rmsnorm.restype = None
         lib.oracle_max_threads.argtypes = []
         lib.oracle_max_threads.restype = ci
         self.path = path
@@ -159,6 +163,19 @@ class OracleLib:
             self._lib.oracle_combine(y[t].ctypes.data, w[t].ctypes.data, k, H, out[t].ctypes.data)
         return out
 
+    def fused_add_rmsnorm(self, x: np.ndarray, residual: Optional[np.ndarray], weight: np.ndarray,
+                          eps: float = 1e-6):
+        """(normalized x, new residual) as bf16 bits, [T, H] each; residual
+        None is the first layer (the residual is x itself)."""
+        xo = _u16(x).copy()
+        T, H = xo.shape
+        ro = np.empty_like(xo) if residual is None else _u16(residual).copy()
+        w = _u16(weight)
+        assert w.shape == (H,) and ro.shape == (T, H)
+        self._lib.oracle_fused_add_rmsnorm(xo.ctypes.data, ro.ctypes.data, w.ctypes.data, T, H, float(eps),
+                                           int(residual is not None))
+        return xo, ro
+
     def moe_layer(self, x, w_router, w13, w2, k: int, norm_topk_prob: bool = True, bias=None,
                   tokens: Optional[Sequence[int]] = None):
         """The whole layer in fp64 for the listed tokens (default: all).
@@ -255,6 +272,10 @@ def expert_down(*a, **kw):
 
 def combine(*a, **kw):
     return default().combine(*a, **kw)
+
+
+def fused_add_rmsnorm(*a, **kw):
+    return default().fused_add_rmsnorm(*a, **kw)
 
 
 def moe_layer(*a, **kw):

@@ -18,6 +18,14 @@
  *   [Linear]  handbook page "The op layer: BaseOP and the layers", section
  *             "Linear layers" (a linear layer is F.linear: y = x W^T + b; the
  *             MoE router is the replicated, unsharded one).
+ *   [Norm]    handbook page "The op layer: BaseOP and the layers": section
+ *             "Ops: reference implementations and dispatch" (rmsnorm computes
+ *             in fp32, casts the normalized value back to the input dtype,
+ *             then multiplies by the weight; fused_add_rmsnorm adds x into
+ *             the residual in place, then normalizes the residual into x) and
+ *             section "RMSNorm and the residual" (the fused op returns the
+ *             normalized result and the new residual; without a residual, x
+ *             is the residual).
  *   [Models]  handbook page "Models and weight loading" (模型与权重加载):
  *             section "ModelConfig" (num_experts, num_experts_per_tok,
  *             moe_intermediate_size, norm_topk_prob), section "Model
@@ -241,5 +249,53 @@ void oracle_moe_layer(const uint16_t* x, const uint16_t* wr, const float* bias, 
         free(y);
         free(ids);
         free(w);
+    }
+}
+
+/* Round a finite double to the nearest bf16 value, ties to even (used where
+ * [Norm] casts to the bf16 model dtype). */
+static double round_bf16(double v) {
+    if (v == 0.0) return v;
+    int e;
+    double m = frexp(v, &e); /* v = m * 2^e, 0.5 <= |m| < 1 */
+    return ldexp(rint(m * 256.0), e - 8);
+}
+
+static uint16_t bf16_bits_of(double v) { /* v already representable in bf16 */
+    float f = (float)v;
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    return (uint16_t)(u >> 16);
+}
+
+/* Fused residual add + RMSNorm [Norm], in place on [T, H] bf16 rows:
+ * with a residual, residual <- bf16(fp32(residual) + fp32(x)) (the add of two
+ * bf16 tensors); without one (first layer), residual <- x. Then, per row,
+ * ms = mean(r^2), n = bf16(r / sqrt(ms + eps)), x <- bf16(w * n) (the
+ * product of two bf16 values, exact in fp32, rounded once). The mean and the
+ * square root are taken in float64. */
+void oracle_fused_add_rmsnorm(uint16_t* x, uint16_t* residual, const uint16_t* weight, int64_t T, int64_t H,
+                              double eps, int has_residual) {
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+        uint16_t* xr = x + t * H;
+        uint16_t* rr = residual + t * H;
+        double ss = 0.0;
+        for (int64_t h = 0; h < H; ++h) {
+            double r;
+            if (has_residual) {
+                float sum = (float)bf16_value(rr[h]) + (float)bf16_value(xr[h]);
+                r = round_bf16((double)sum);
+            } else {
+                r = bf16_value(xr[h]);
+            }
+            rr[h] = bf16_bits_of(r);
+            ss += r * r;
+        }
+        const double inv = 1.0 / sqrt(ss / (double)H + eps);
+        for (int64_t h = 0; h < H; ++h) {
+            const double n = round_bf16(bf16_value(rr[h]) * inv);
+            xr[h] = bf16_bits_of(round_bf16((double)(float)(bf16_value(weight[h]) * n)));
+        }
     }
 }

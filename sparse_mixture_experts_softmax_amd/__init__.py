@@ -21,6 +21,7 @@ from ._lib import (  # noqa: F401
     moe_align_capacity,
     moe_align_workspace_bytes,
     moe_combine,
+    moe_fused_add_rmsnorm,
     moe_grouped_gemm_down,
     moe_grouped_gemm_gate_up_silu,
     moe_last_error,
@@ -29,4 +30,4 @@ from ._lib import (  # noqa: F401
     moe_pick_block_m,
     moe_route,
 )
-from .layer import MoEBuffers, MoEConfig, PackedExperts, allocate, moe_layer, pack_experts  # noqa: F401
+from .layer import MoEBuffers, MoEConfig, PackedExperts, allocate, gated_mlp, moe_layer, pack_experts  # noqa: F401

@@ -39,6 +39,7 @@ EXPORTS = (
     "moe_pick_block_m",
     "moe_packed_weight_bytes",
     "moe_pack_weights",
+    "moe_fused_add_rmsnorm",
 )
 
 
@@ -75,6 +76,8 @@ def lib():
         L.moe_pick_block_m.argtypes, L.moe_pick_block_m.restype = [i64, i32, i32], i32
         L.moe_packed_weight_bytes.argtypes, L.moe_packed_weight_bytes.restype = [i32, i32, i32], sz
         L.moe_pack_weights.argtypes, L.moe_pack_weights.restype = [p, p, i32, i32, i32, i32, p], ctypes.c_int
+        L.moe_fused_add_rmsnorm.argtypes = [p, p, p, i64, i32, ctypes.c_float, i32, p]
+        L.moe_fused_add_rmsnorm.restype = ctypes.c_int
         for name in ("moe_route", "moe_align_by_expert", "moe_grouped_gemm_gate_up_silu", "moe_grouped_gemm_down",
                      "moe_combine"):
             getattr(L, name).restype = ctypes.c_int
@@ -157,6 +160,13 @@ def moe_pack_weights(w, w_packed, E: int, N: int, K: int, gated: bool, stream=No
     bf = torch.bfloat16
     _check(lib().moe_pack_weights(_dev(w, bf, "w"), _dev(w_packed, bf, "w_packed"), E, N, K, int(bool(gated)),
                                   _stream(stream, w)))
+
+
+def moe_fused_add_rmsnorm(x, residual, weight, T: int, H: int, eps: float, has_residual: bool, stream=None):
+    """In place: residual <- residual + x (or x), x <- rmsnorm(residual)."""
+    bf = torch.bfloat16
+    _check(lib().moe_fused_add_rmsnorm(_dev(x, bf, "x"), _dev(residual, bf, "residual"), _dev(weight, bf, "weight"),
+                                       T, H, float(eps), int(bool(has_residual)), _stream(stream, x)))
 
 
 def moe_align_by_expert(topk_ids, T: int, k: int, E: int, block_m: int, sorted_ids, block_expert, expert_counts,

@@ -23,7 +23,7 @@ LIB_NAME = "libmoe_mi355x.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 ARCH = "gfx950"
 
-SOURCES = ["abi.cpp", "route.hip", "align.hip", "pack.hip", "gemm.hip", "combine.hip"]
+SOURCES = ["abi.cpp", "route.hip", "align.hip", "pack.hip", "gemm.hip", "combine.hip", "rmsnorm.hip"]
 HIP_FLAGS = [
     f"--offload-arch={ARCH}",
     "-O3",

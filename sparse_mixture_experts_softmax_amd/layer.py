@@ -140,3 +140,30 @@ def moe_layer(x: torch.Tensor, w_router: torch.Tensor, w13: Optional[torch.Tenso
                                b.y, s)
     _lib.moe_combine(b.y, b.topk_weights, T, k, H, b.out, s)
     return b.out
+
+
+def gated_mlp(x: torch.Tensor, packed: PackedExperts, *, block_m: Optional[int] = None, out_dtype=torch.bfloat16,
+              stream=None) -> torch.Tensor:
+    """Dense SwiGLU GatedMLP (down(silu(gate(x)) * up(x)), the "Models and
+    weight loading" page's GatedMLP) through the same grouped GEMMs: every
+    token is routed to the single expert of ``packed`` (num_experts == 1)
+    with weight 1, so the grouping is the identity and the combine is a copy
+    to the output dtype. Used for dense layers and mlp_only_layers."""
+    if packed.num_experts != 1:
+        raise ValueError("gated_mlp needs a single packed expert (E = 1)")
+    if x.dim() != 2 or x.shape[1] != packed.hidden_size:
+        raise ValueError(f"x must be [T, {packed.hidden_size}]")
+    T, H = x.shape
+    I = packed.intermediate_size
+    b = allocate(T, H, 1, 1, I, x.device, block_m, out_dtype)
+    s = _lib._stream(stream, x)
+    ids = torch.zeros((T, 1), dtype=torch.int32, device=x.device)
+    ones = torch.ones((T, 1), dtype=torch.float32, device=x.device)
+    _lib.moe_align_by_expert(ids, T, 1, 1, b.block_m, b.sorted_ids, b.block_expert, b.expert_counts, b.num_padded,
+                             b.workspace, s)
+    _lib.moe_grouped_gemm_gate_up_silu(x, packed.w13, b.sorted_ids, b.block_expert, b.num_padded, T, 1, H, I, 1,
+                                       b.block_m, b.cap, b.act, s)
+    _lib.moe_grouped_gemm_down(b.act, packed.w2, b.sorted_ids, b.block_expert, b.num_padded, T, 1, H, I, 1,
+                               b.block_m, b.cap, b.y, s)
+    _lib.moe_combine(b.y, ones, T, 1, H, b.out, s)
+    return b.out

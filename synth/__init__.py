@@ -150,6 +150,9 @@ CONFIGS = {
     "prefill": MoEShape("prefill", 4096, 2048, 128, 8, 768),
     "skewed": MoEShape("skewed", 16384, 2048, 128, 8, 768, skewed=True),
     "large": MoEShape("large", 8192, 4096, 128, 8, 1536),
+    # Dense SwiGLU MLP of the Qwen3-0.6B layer the op-layer page prints
+    # (gate_up_proj (6144, 1024), down_proj (1024, 3072)): one expert, k = 1.
+    "dense": MoEShape("dense", 4096, 1024, 1, 1, 3072),
 }
 
 

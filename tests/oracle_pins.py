@@ -321,6 +321,56 @@ def pin_token_subset(orc):
     assert np.array_equal(o2, out[sub]) and np.array_equal(i2, ids[sub]) and np.array_equal(w2, w[sub])
 
 
+# ----------------------------------------------------------------------------
+# Fused residual add + RMSNorm (the step before the layer)
+# ----------------------------------------------------------------------------
+def pin_rmsnorm_worked_example(orc):
+    fx = json.load(open(os.path.join(GOLDEN, "rmsnorm_worked_example.json")))
+    for case in fx["cases"]:
+        x = bf16_bits(case["x"])
+        r = None if case["residual"] is None else bf16_bits(case["residual"])
+        out, res = orc.fused_add_rmsnorm(x, r, bf16_bits(case["weight"]), fx["eps"])
+        assert synth.bf16_to_f64(out).tolist() == case["out"], (case["derivation"], synth.bf16_to_f64(out))
+        assert synth.bf16_to_f64(res).tolist() == case["new_residual"]
+
+
+def pin_rmsnorm_library(orc):
+    """torch.nn.functional.rms_norm (float64) on the new residual, times the
+    weight, agrees with the oracle to within the two bf16 roundings."""
+    for T, H, scale in ((7, 64, 1.0), (5, 2048, 3.0), (3, 96, 1e-4)):
+        x = synth.normal_bf16(T * H, 77, (T, H), scale)
+        r = synth.normal_bf16(T * H, 78, (T, H), scale)
+        w = synth.normal_bf16(H, 79, (H,), 1.0)
+        out, res = orc.fused_add_rmsnorm(x, r, w, 1e-6)
+        r64 = torch.from_numpy(synth.bf16_to_f64(res))
+        n = F.rms_norm(r64, (H,), eps=1e-6)
+        ref = (n * torch.from_numpy(synth.bf16_to_f64(w))).numpy()
+        got = synth.bf16_to_f64(out)
+        assert (np.abs(got - ref) <= 2.0 ** -7 * np.abs(ref) + 1e-30).all()
+        # the residual is the bf16 rounding of the fp32 sum
+        s32 = (synth.bf16_to_f64(x).astype(np.float32) + synth.bf16_to_f64(r).astype(np.float32))
+        ref_r = torch.from_numpy(s32).to(torch.bfloat16).float().numpy()
+        assert np.array_equal(synth.bf16_to_f64(res), ref_r)
+
+
+def pin_rmsnorm_closed_forms(orc):
+    H = 64
+    w = bf16_bits(np.ones(H))
+    # constant rows: n = c / sqrt(c^2 + eps)
+    for c, want in ((1.0, 1.0), (-2.0, -1.0), (2.0 ** -12, None)):
+        out, res = orc.fused_add_rmsnorm(bf16_bits(np.full((1, H), c)), None, w, 1e-6)
+        got = synth.bf16_to_f64(out)[0]
+        if want is None:  # eps dominates: 2^-12 / sqrt(2^-24 + 1e-6)
+            want = float(torch.tensor(2.0 ** -12 / np.sqrt(2.0 ** -24 + 1e-6)).to(torch.bfloat16))
+        assert (got == want).all(), (c, got[0], want)
+        assert np.array_equal(res, bf16_bits(np.full((1, H), c)))
+    # scaling x by a power of two leaves the normalized output unchanged (eps aside)
+    x = synth.normal_bf16(5, 80, (4, H), 1.0)
+    a, _ = orc.fused_add_rmsnorm(x, None, w, 0.0)
+    b, _ = orc.fused_add_rmsnorm((x.astype(np.uint32) + (3 << 7)).astype(np.uint16), None, w, 0.0)
+    assert np.array_equal(a, b)
+
+
 ALL_PINS = [
     pin_worked_example,
     pin_printed_shapes,
@@ -334,4 +384,7 @@ ALL_PINS = [
     pin_linearity,
     pin_relabel,
     pin_token_subset,
+    pin_rmsnorm_worked_example,
+    pin_rmsnorm_library,
+    pin_rmsnorm_closed_forms,
 ]

@@ -112,6 +112,18 @@ def test_pack_validation():
     assert L.moe_pack_weights(NULL, other, 2, 32, 64, 0, NULL) == _lib.MOE_ERR_INVALID
 
 
+def test_rmsnorm_validation():
+    L = _raw()
+    other = ctypes.c_void_p(0x2000)
+    f = L.moe_fused_add_rmsnorm
+    assert f(FAKE, other, FAKE, 4, 12, ctypes.c_float(1e-6), 1, NULL) == _lib.MOE_ERR_UNSUPPORTED
+    assert f(FAKE, other, FAKE, 4, 8 * 2048 + 8, ctypes.c_float(1e-6), 1, NULL) == _lib.MOE_ERR_UNSUPPORTED
+    assert f(FAKE, other, FAKE, 4, 64, ctypes.c_float(-1.0), 1, NULL) == _lib.MOE_ERR_INVALID
+    assert f(FAKE, FAKE, FAKE, 4, 64, ctypes.c_float(1e-6), 1, NULL) == _lib.MOE_ERR_INVALID  # aliasing
+    assert f(NULL, other, FAKE, 4, 64, ctypes.c_float(1e-6), 1, NULL) == _lib.MOE_ERR_INVALID
+    assert f(NULL, NULL, NULL, 0, 64, ctypes.c_float(1e-6), 1, NULL) == _lib.MOE_OK
+
+
 def test_combine_validation():
     L = _raw()
     assert L.moe_combine(FAKE, FAKE, 4, 2, 64, FAKE, 7, NULL) == _lib.MOE_ERR_INVALID

@@ -36,6 +36,14 @@ MUTANTS = [
      "for (int64_t i = n - 1; i >= 0; --i)\n            if (ids[i] == e) sorted_ids[fill++] = (int32_t)i;"),
     ("align_no_padding", "int64_t padded = (counts[e] + block_m - 1) / block_m * block_m;",
      "int64_t padded = counts[e];"),
+    ("norm_eps_dropped", "const double inv = 1.0 / sqrt(ss / (double)H + eps);",
+     "const double inv = 1.0 / sqrt(ss / (double)H);"),
+    ("norm_sum_not_mean", "const double inv = 1.0 / sqrt(ss / (double)H + eps);",
+     "const double inv = 1.0 / sqrt(ss + eps);"),
+    ("norm_cast_after_weight", "const double n = round_bf16(bf16_value(rr[h]) * inv);",
+     "const double n = bf16_value(rr[h]) * inv;"),
+    ("norm_residual_not_added", "float sum = (float)bf16_value(rr[h]) + (float)bf16_value(xr[h]);",
+     "float sum = (float)bf16_value(xr[h]);"),
     ("align_sentinel_zero", "for (int64_t r = 0; r < cap; ++r) sorted_ids[r] = (int32_t)n;",
      "for (int64_t r = 0; r < cap; ++r) sorted_ids[r] = 0;"),
 ]
