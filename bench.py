@@ -357,7 +357,7 @@ def main():
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4)}
     roof["kernel"] = ("moe_grouped_gemm_gate_up_silu: " +
-                      {16: "grouped_gemm_skinny_kernel<true,4,2,8>", 32: "grouped_gemm_kernel<GemmCfg<32,128,true>>",
+                      {16: "grouped_gemm_skinny_kernel<true,1,2,8>", 32: "grouped_gemm_kernel<GemmCfg<32,128,true>>",
                        64: "grouped_gemm_wide_kernel<WideCfg<true,64,4>>",
                        128: "grouped_gemm_wide_kernel<WideCfg<true,128,3>>"}[block_m])
     roof["kernel_ms"] = round(dom_ms, 5)

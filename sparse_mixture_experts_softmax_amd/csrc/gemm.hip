@@ -569,8 +569,10 @@ template <bool GATED>
 static int launch_skinny(const void* a, const void* w, const int32_t* sorted_ids, const int32_t* block_expert,
                          const int32_t* num_padded, int k, int64_t n_pairs, int K, int N_out, int64_t cap, void* out,
                          hipStream_t s, const char* what) {
+    // Chosen by sweeps on the decode-shaped layer: single-wave workgroups
+    // (finest load balance) for gate/up; the down shape is insensitive.
     if (GATED)
-        return launch_skinny_cfg<true, 4, 2, 8>(a, w, sorted_ids, block_expert, num_padded, k, n_pairs, K, N_out, cap,
+        return launch_skinny_cfg<true, 1, 2, 8>(a, w, sorted_ids, block_expert, num_padded, k, n_pairs, K, N_out, cap,
                                                 out, s, what);
     return launch_skinny_cfg<false, 4, 4, 4>(a, w, sorted_ids, block_expert, num_padded, k, n_pairs, K, N_out, cap,
                                              out, s, what);
