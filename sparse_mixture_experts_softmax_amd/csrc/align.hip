@@ -2,7 +2,9 @@
 // padded to the GEMM row tile, stable (ascending flat index inside a group)
 // and deterministic.
 //
-// The flat pairs are cut into tiles of kAlignTile entries. Kernel 1 counts
+// The flat pairs are cut into at most kAlignMaxTiles tiles of at least
+// kAlignMinTile entries (a multiple of 256); every tile's workgroup reads all
+// tiles' counts, so the tile count is kept small. Kernel 1 counts
 // each tile's pairs per expert into the workspace (LDS atomics: the counts do
 // not depend on their order). Kernel 2 runs one workgroup per tile: it reads
 // every tile's counts, forms the expert totals, the padded exclusive scan and
@@ -19,17 +21,18 @@
 
 namespace moe {
 
-constexpr int kAlignTile = 4096;
+constexpr int kAlignMinTile = 1024;
+constexpr int kAlignMaxTiles = 32;
 constexpr int kAlignThreads = 256;
 constexpr int kAlignWaves = kAlignThreads / kWave;
 
-__global__ __launch_bounds__(kAlignThreads) void align_hist_kernel(const int32_t* __restrict__ ids, int64_t n, int E,
-                                                                   int32_t* __restrict__ ws) {
+__global__ __launch_bounds__(kAlignThreads) void align_hist_kernel(const int32_t* __restrict__ ids, int64_t n,
+                                                                   int64_t tile_size, int E, int32_t* __restrict__ ws) {
     __shared__ int cnt[kMaxExperts];
     for (int e = threadIdx.x; e < E; e += blockDim.x) cnt[e] = 0;
     __syncthreads();
-    const int64_t start = (int64_t)blockIdx.x * kAlignTile;
-    const int64_t end = min(n, start + kAlignTile);
+    const int64_t start = (int64_t)blockIdx.x * tile_size;
+    const int64_t end = min(n, start + tile_size);
     for (int64_t i = start + threadIdx.x; i < end; i += blockDim.x) {
         const int e = ids[i];
         if ((unsigned)e < (unsigned)E) atomicAdd(&cnt[e], 1);
@@ -58,7 +61,7 @@ __device__ int block_inclusive_scan(int v, int* wave_tot, int E) {
 }
 
 __global__ __launch_bounds__(kAlignThreads) void align_scatter_kernel(
-    const int32_t* __restrict__ ids, int64_t n, int E, int BM, int64_t cap, int ntiles,
+    const int32_t* __restrict__ ids, int64_t n, int64_t tile_size, int E, int BM, int64_t cap, int ntiles,
     const int32_t* __restrict__ ws, int fused_hist, int32_t* __restrict__ sorted_ids,
     int32_t* __restrict__ block_expert, int32_t* __restrict__ counts_out, int32_t* __restrict__ num_padded) {
     __shared__ int total[kMaxExperts];    // c_e
@@ -69,8 +72,8 @@ __global__ __launch_bounds__(kAlignThreads) void align_scatter_kernel(
     const int tid = threadIdx.x;
     const int lane = tid % kWave, wave = tid / kWave;
     const int tile = blockIdx.x;
-    const int64_t start = (int64_t)tile * kAlignTile;
-    const int64_t end = min(n, start + kAlignTile);
+    const int64_t start = (int64_t)tile * tile_size;
+    const int64_t end = min(n, start + tile_size);
 
     if (fused_hist) {
         for (int e = tid; e < kMaxExperts; e += blockDim.x) total[e] = 0;
@@ -158,7 +161,17 @@ __global__ __launch_bounds__(kAlignThreads) void align_scatter_kernel(
     }
 }
 
-static int64_t align_ntiles(int64_t T, int32_t k) { return (T * k + kAlignTile - 1) / kAlignTile; }
+// Entries per tile (a multiple of 256) and the resulting tile count.
+static int64_t align_tile_size(int64_t T, int32_t k) {
+    const int64_t n = T * k;
+    int64_t t = (n + kAlignMaxTiles - 1) / kAlignMaxTiles;
+    t = (t + 255) / 256 * 256;
+    return t < kAlignMinTile ? kAlignMinTile : t;
+}
+static int64_t align_ntiles(int64_t T, int32_t k) {
+    const int64_t ts = align_tile_size(T, k);
+    return (T * k + ts - 1) / ts;
+}
 
 }  // namespace moe
 
@@ -200,13 +213,13 @@ extern "C" int moe_align_by_expert(const int32_t* topk_ids, int64_t T, int32_t k
     const int64_t n = T * k;
     hipStream_t s = (hipStream_t)stream;
     if (ntiles > 1) {
-        hipLaunchKernelGGL(align_hist_kernel, dim3((unsigned)ntiles), dim3(kAlignThreads), 0, s, topk_ids, n, (int)E,
-                           (int32_t*)workspace);
+        hipLaunchKernelGGL(align_hist_kernel, dim3((unsigned)ntiles), dim3(kAlignThreads), 0, s, topk_ids, n,
+                           align_tile_size(T, k), (int)E, (int32_t*)workspace);
         int rc = check_launch("moe_align_by_expert (histogram)");
         if (rc) return rc;
     }
-    hipLaunchKernelGGL(align_scatter_kernel, dim3((unsigned)ntiles), dim3(kAlignThreads), 0, s, topk_ids, n, (int)E,
-                       (int)block_m, cap, (int)ntiles, (const int32_t*)workspace, (int)(ntiles <= 1), sorted_ids,
+    hipLaunchKernelGGL(align_scatter_kernel, dim3((unsigned)ntiles), dim3(kAlignThreads), 0, s, topk_ids, n,
+                       align_tile_size(T, k), (int)E, (int)block_m, cap, (int)ntiles, (const int32_t*)workspace, (int)(ntiles <= 1), sorted_ids,
                        block_expert, expert_counts, num_padded);
     return check_launch("moe_align_by_expert (scatter)");
 }

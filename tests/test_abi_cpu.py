@@ -38,7 +38,9 @@ def test_capacity_and_workspace():
     assert moe.moe_align_capacity(0, 8, 128, 64) == 0
     assert moe.moe_align_capacity(10, 2, 8, 48) == -1
     assert moe.moe_align_workspace_bytes(64, 8, 128, 16) == 0  # one tile: no workspace
-    assert moe.moe_align_workspace_bytes(16384, 8, 128, 64) == 32 * 128 * 4
+    assert moe.moe_align_workspace_bytes(16384, 8, 128, 64) == 32 * 128 * 4  # 32 tiles of 4096 pairs
+    assert moe.moe_align_workspace_bytes(4096, 8, 128, 64) == 32 * 128 * 4  # 32 tiles of 1024 pairs
+    assert moe.moe_align_workspace_bytes(128, 8, 128, 64) == 0  # one tile
     for T, k, E in ((64, 8, 128), (4096, 8, 128), (16, 2, 8)):
         assert moe.moe_pick_block_m(T, k, E) in (16, 32, 64, 128)
 
