@@ -262,6 +262,7 @@ struct WideCfg {
     static_assert(COPIES % (WAVES_M * WAVES_N) == 0, "copies must split evenly over the waves");
     static_assert(STAGES >= 2 && STAGES <= 5, "stages");
     static_assert(STAGES * STAGE_BYTES <= 160 * 1024, "LDS");
+    static_assert(THREADS >= BM, "one row id per thread");
 };
 
 template <class C>
@@ -289,6 +290,7 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_wide_kernel(
 
     const int32_t* ids_blk = sorted_ids + (int64_t)mb * BM;
     auto real_row = [&](int32_t id) { return id >= 0 && (int64_t)id < n_pairs; };
+    const int32_t my_id = tid < BM ? ids_blk[tid] : 0;  // row ids for the epilogue (C::THREADS >= BM)
 
     // This wave's copies: index q over [A rows 16q.. | B band q - BM/16].
     const uint16_t* src[C::COPIES_PER_WAVE];
@@ -383,8 +385,15 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_wide_kernel(
         }
     }
 
+    // The stages are free once every wave is done with the last one: they
+    // now hold the block's row ids.
+    __syncthreads();
+    int32_t* ids_s = (int32_t*)smem;
+    if (tid < BM) ids_s[tid] = my_id;
+    __syncthreads();
+
     // Epilogue: element q of a 32x32 tile is row 8*(q/4) + 4*(lane/32) + q%4,
-    // column lane%32.
+    // column lane%32; the ids of rows q..q+3 come as one 16-byte LDS read.
     if (C::GATED) {
 #pragma unroll
         for (int g = 0; g < C::TN / 2; ++g) {
@@ -393,10 +402,17 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_wide_kernel(
 #pragma unroll
             for (int i = 0; i < C::TM; ++i)
 #pragma unroll
-                for (int q = 0; q < 16; ++q) {
-                    const int row = wm * 64 + i * 32 + 8 * (q / 4) + 4 * (lane / 32) + q % 4;
-                    const float v = real_row(ids_blk[row]) ? silu(acc[i][g][q]) * acc[i][g + C::TN / 2][q] : 0.f;
-                    ((uint16_t*)out)[((int64_t)mb * BM + row) * N_out + col] = f32_to_bf16(v);
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    const int row0 = wm * 64 + i * 32 + 8 * q4 + 4 * (lane / 32);
+                    const int4 id4 = *(const int4*)&ids_s[row0];
+                    const int32_t ids[4] = {id4.x, id4.y, id4.z, id4.w};
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const int q = 4 * q4 + u;
+                        const float v = silu(acc[i][g][q]) * acc[i][g + C::TN / 2][q];
+                        ((uint16_t*)out)[((int64_t)mb * BM + row0 + u) * N_out + col] =
+                            f32_to_bf16(real_row(ids[u]) ? v : 0.f);
+                    }
                 }
         }
     } else {
@@ -407,10 +423,13 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_wide_kernel(
 #pragma unroll
             for (int i = 0; i < C::TM; ++i)
 #pragma unroll
-                for (int q = 0; q < 16; ++q) {
-                    const int row = wm * 64 + i * 32 + 8 * (q / 4) + 4 * (lane / 32) + q % 4;
-                    const int32_t id = ids_blk[row];
-                    if (real_row(id)) ((float*)out)[(int64_t)id * N_out + col] = acc[i][t][q];
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    const int row0 = wm * 64 + i * 32 + 8 * q4 + 4 * (lane / 32);
+                    const int4 id4 = *(const int4*)&ids_s[row0];
+                    const int32_t ids[4] = {id4.x, id4.y, id4.z, id4.w};
+#pragma unroll
+                    for (int u = 0; u < 4; ++u)
+                        if (real_row(ids[u])) ((float*)out)[(int64_t)ids[u] * N_out + col] = acc[i][t][4 * q4 + u];
                 }
         }
     }

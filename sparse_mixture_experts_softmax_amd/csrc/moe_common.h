@@ -70,6 +70,15 @@ __device__ __forceinline__ void vm_wait() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// Workgroup barrier for LDS only: waits for this wave's LDS accesses, then
+// s_barrier; the fences (LDS address space, workgroup scope) keep the
+// compiler from moving LDS accesses across it without waiting on global loads.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
 
 template <typename T>
