@@ -9,9 +9,10 @@
 // depend on scheduling. Small batches use one expert tile per workgroup (many
 // workgroups pull the router weight in parallel); large ones use eight, so
 // the activation rows are re-read less often. route_topk_kernel: one wave
-// per token; each lane holds up to four of the token's logits, and the
-// softmax max, the softmax sum and each of the k arg-max rounds are wave
-// reductions. Selection uses the fp32 logits, so it is exact given them.
+// per token; each lane holds up to four of the token's logits, and each of
+// the k arg-max rounds and the softmax sums are wave reductions on DPP lane
+// permutations (no LDS). Selection uses the fp32 logits, so it is exact given
+// them.
 #include "abi_util.h"
 #include "moe_common.h"
 
@@ -84,14 +85,77 @@ __global__ __launch_bounds__(kRouteSlices* kWave) void router_logits_kernel(cons
     }
 }
 
-struct ArgMax {
-    float v;
-    int i;
-};
+// Wave-wide reductions without LDS traffic: DPP lane permutations inside
+// each row of 16 lanes (xor 1, xor 2, mirror within 8, mirror within 16)
+// leave every lane holding its row's result; the four row results are then
+// read with v_readlane and combined in a fixed order.
+constexpr int kDppXor1 = 0xB1;         // quad_perm(1,0,3,2)
+constexpr int kDppXor2 = 0x4E;         // quad_perm(2,3,0,1)
+constexpr int kDppHalfMirror = 0x141;  // lane i <- 7 - i within each 8
+constexpr int kDppMirror = 0x140;      // lane i <- 15 - i within each 16
 
-__device__ __forceinline__ ArgMax better(ArgMax a, ArgMax b) {
-    // larger value first; equal values -> lower expert index first
-    return (b.v > a.v || (b.v == a.v && b.i < a.i)) ? b : a;
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+
+template <int CTRL>
+__device__ __forceinline__ uint64_t max_dpp(uint64_t v) {
+    const uint64_t o = ((uint64_t)dpp_u32<CTRL>((uint32_t)(v >> 32)) << 32) | dpp_u32<CTRL>((uint32_t)v);
+    return o > v ? o : v;
+}
+
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int lane) {
+    return ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(v >> 32), lane) << 32) |
+           (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, lane);
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+    v = max_dpp<kDppXor1>(v);
+    v = max_dpp<kDppXor2>(v);
+    v = max_dpp<kDppHalfMirror>(v);
+    v = max_dpp<kDppMirror>(v);
+    uint64_t m = readlane_u64(v, 0);
+#pragma unroll
+    for (int r = 1; r < 4; ++r) {
+        const uint64_t o = readlane_u64(v, 16 * r);
+        m = o > m ? o : m;
+    }
+    return m;
+}
+
+template <int CTRL>
+__device__ __forceinline__ float add_dpp(float v) {
+    return v + __uint_as_float(dpp_u32<CTRL>(__float_as_uint(v)));
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+    v = add_dpp<kDppXor1>(v);
+    v = add_dpp<kDppXor2>(v);
+    v = add_dpp<kDppHalfMirror>(v);
+    v = add_dpp<kDppMirror>(v);
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+    return (r0 + r1) + (r2 + r3);
+}
+
+// Selection key of (logit, expert): the logit's bits mapped to an unsigned
+// integer of the same order in the high word (-0 taken as +0), the
+// complemented expert index in the low word, so the largest key is the
+// largest logit and, among equal logits, the lowest expert. NaN logits rank
+// below every number (high word 0); key 0 marks an expert already taken or
+// past E.
+__device__ __forceinline__ uint64_t select_key(float v, int e) {
+    const uint32_t u = v == 0.f ? 0u : __float_as_uint(v);
+    const uint32_t ord = (u & 0x7fffffffu) > 0x7f800000u ? 0u : ((u & 0x80000000u) ? ~u : (u | 0x80000000u));
+    return ((uint64_t)ord << 32) | (uint32_t)~e;
+}
+
+__device__ __forceinline__ float key_logit(uint64_t key) {
+    const uint32_t ord = (uint32_t)(key >> 32);
+    return __uint_as_float((ord & 0x80000000u) ? (ord & 0x7fffffffu) : ~ord);
 }
 
 __global__ __launch_bounds__(kTopkWaves* kWave) void route_topk_kernel(const float* __restrict__ logits,
@@ -103,50 +167,41 @@ __global__ __launch_bounds__(kTopkWaves* kWave) void route_topk_kernel(const flo
     if (t >= T) return;
     const float* row = logits + t * E;
     float v[4];
-    bool live[4];
-    float mx = -INFINITY;
+    uint64_t key[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int e = lane + i * kWave;
-        live[i] = e < E;
-        v[i] = live[i] ? row[e] : -INFINITY;
-        mx = fmaxf(mx, v[i]);
+        v[i] = row[min(e, E - 1)];
+        key[i] = e < E ? select_key(v[i], e) : 0;
     }
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) mx = fmaxf(mx, wave_shfl_xor(mx, m));
-    float z = 0.f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) z += live[i] ? expf(v[i] - mx) : 0.f;
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) z += wave_shfl_xor(z, m);
-
+    // k rounds of a wave arg-max; lane j keeps the j-th pick
     int my_id = 0;
     float my_val = 0.f;
     for (int j = 0; j < k; ++j) {
-        ArgMax best{-INFINITY, 0x7fffffff};
+        uint64_t best = key[0];
+#pragma unroll
+        for (int i = 1; i < 4; ++i) best = key[i] > best ? key[i] : best;
+        best = wave_max_u64(best);
+        const int e = (int)~(uint32_t)best;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            if (live[i]) best = better(best, ArgMax{v[i], lane + i * kWave});
-#pragma unroll
-        for (int m = 32; m >= 1; m >>= 1) {
-            ArgMax o{wave_shfl_xor(best.v, m), wave_shfl_xor(best.i, m)};
-            best = better(best, o);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            if (lane + i * kWave == best.i) live[i] = false;
+            if (lane + i * kWave == e) key[i] = 0;
         if (lane == j) {
-            my_id = best.i;
-            my_val = best.v;
+            my_id = e;
+            my_val = key_logit(best);
         }
     }
+    // softmax: the largest logit is the first pick
+    const float mx = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_val), 0));
     const float ex = lane < k ? expf(my_val - mx) : 0.f;
-    float denom = z;
+    float denom;
     if (norm) {
-        float sel_sum = ex;
+        denom = wave_sum(ex);
+    } else {
+        float z = 0.f;
 #pragma unroll
-        for (int m = 32; m >= 1; m >>= 1) sel_sum += wave_shfl_xor(sel_sum, m);
-        denom = sel_sum;
+        for (int i = 0; i < 4; ++i) z += lane + i * kWave < E ? expf(v[i] - mx) : 0.f;
+        denom = wave_sum(z);
     }
     if (lane < k) {
         topk_ids[t * k + lane] = my_id;
