@@ -2,9 +2,10 @@
 // padded to the GEMM row tile, stable (ascending flat index inside a group)
 // and deterministic.
 //
-// The flat pairs are cut into at most kAlignMaxTiles tiles of at least
-// kAlignMinTile entries (a multiple of 256); every tile's workgroup reads all
-// tiles' counts, so the tile count is kept small. Kernel 1 counts
+// The flat pairs are cut into tiles of 1024, 2048 or 4096 entries (the
+// smallest giving at most 32 tiles, since every tile's workgroup reads all
+// tiles' counts); each thread loads its (at most 16) ids of the tile at once,
+// so a kernel waits for memory once. Kernel 1 counts
 // each tile's pairs per expert into the workspace (LDS atomics: the counts do
 // not depend on their order). Kernel 2 runs one workgroup per tile: it reads
 // every tile's counts, forms the expert totals, the padded exclusive scan and
@@ -21,22 +22,40 @@
 
 namespace moe {
 
-constexpr int kAlignMinTile = 1024;
 constexpr int kAlignMaxTiles = 32;
 constexpr int kAlignThreads = 256;
 constexpr int kAlignWaves = kAlignThreads / kWave;
 
-__global__ __launch_bounds__(kAlignThreads) void align_hist_kernel(const int32_t* __restrict__ ids, int64_t n,
-                                                                   int64_t tile_size, int E, int32_t* __restrict__ ws) {
+// Entry q of this thread in tile `tile` (PT entries per thread): flat index
+// tile*PT*256 + q*256 + tid. All PT loads are issued before any is used;
+// entries past n read entry n-1 and are marked -1.
+template <int PT>
+__device__ __forceinline__ void load_tile_ids(const int32_t* __restrict__ ids, int64_t n, int E, int tile,
+                                              int (&e)[PT]) {
+    const int64_t start = (int64_t)tile * PT * kAlignThreads + threadIdx.x;
+#pragma unroll
+    for (int q = 0; q < PT; ++q) {
+        const int64_t i = start + q * kAlignThreads;
+        e[q] = ids[min(i, n - 1)];
+    }
+#pragma unroll
+    for (int q = 0; q < PT; ++q) {
+        const int64_t i = start + q * kAlignThreads;
+        if (i >= n || (unsigned)e[q] >= (unsigned)E) e[q] = -1;
+    }
+}
+
+template <int PT>
+__global__ __launch_bounds__(kAlignThreads) void align_hist_kernel(const int32_t* __restrict__ ids, int64_t n, int E,
+                                                                   int32_t* __restrict__ ws) {
     __shared__ int cnt[kMaxExperts];
+    int my[PT];
+    load_tile_ids<PT>(ids, n, E, blockIdx.x, my);
     for (int e = threadIdx.x; e < E; e += blockDim.x) cnt[e] = 0;
     __syncthreads();
-    const int64_t start = (int64_t)blockIdx.x * tile_size;
-    const int64_t end = min(n, start + tile_size);
-    for (int64_t i = start + threadIdx.x; i < end; i += blockDim.x) {
-        const int e = ids[i];
-        if ((unsigned)e < (unsigned)E) atomicAdd(&cnt[e], 1);
-    }
+#pragma unroll
+    for (int q = 0; q < PT; ++q)
+        if (my[q] >= 0) atomicAdd(&cnt[my[q]], 1);
     __syncthreads();
     for (int e = threadIdx.x; e < E; e += blockDim.x) ws[(int64_t)blockIdx.x * E + e] = cnt[e];
 }
@@ -60,8 +79,9 @@ __device__ int block_inclusive_scan(int v, int* wave_tot, int E) {
     return x + add;
 }
 
+template <int PT>
 __global__ __launch_bounds__(kAlignThreads) void align_scatter_kernel(
-    const int32_t* __restrict__ ids, int64_t n, int64_t tile_size, int E, int BM, int64_t cap, int ntiles,
+    const int32_t* __restrict__ ids, int64_t n, int E, int BM, int64_t cap, int ntiles,
     const int32_t* __restrict__ ws, int fused_hist, int32_t* __restrict__ sorted_ids,
     int32_t* __restrict__ block_expert, int32_t* __restrict__ counts_out, int32_t* __restrict__ num_padded) {
     __shared__ int total[kMaxExperts];    // c_e
@@ -72,24 +92,33 @@ __global__ __launch_bounds__(kAlignThreads) void align_scatter_kernel(
     const int tid = threadIdx.x;
     const int lane = tid % kWave, wave = tid / kWave;
     const int tile = blockIdx.x;
-    const int64_t start = (int64_t)tile * tile_size;
-    const int64_t end = min(n, start + tile_size);
+    const int64_t start = (int64_t)tile * PT * kAlignThreads;
+    int my[PT];
+    load_tile_ids<PT>(ids, n, E, tile, my);
 
     if (fused_hist) {
         for (int e = tid; e < kMaxExperts; e += blockDim.x) total[e] = 0;
         __syncthreads();
-        for (int64_t i = start + tid; i < end; i += blockDim.x) {
-            const int e = ids[i];
-            if ((unsigned)e < (unsigned)E) atomicAdd(&total[e], 1);
-        }
+#pragma unroll
+        for (int q = 0; q < PT; ++q)
+            if (my[q] >= 0) atomicAdd(&total[my[q]], 1);
         __syncthreads();
         if (tid < E) base[tid] = 0;
     } else if (tid < E) {
+        // every tile's count of expert tid, 32 loads in flight at a time
         int tot = 0, pre = 0;
-        for (int t = 0; t < ntiles; ++t) {
-            const int h = ws[(int64_t)t * E + tid];
-            if (t < tile) pre += h;
-            tot += h;
+        for (int t0 = 0; t0 < ntiles; t0 += kAlignMaxTiles) {
+            int h[kAlignMaxTiles];
+#pragma unroll
+            for (int u = 0; u < kAlignMaxTiles; ++u) h[u] = ws[(int64_t)min(t0 + u, ntiles - 1) * E + tid];
+#pragma unroll
+            for (int u = 0; u < kAlignMaxTiles; ++u) {
+                const int t = t0 + u;
+                if (t < ntiles) {
+                    if (t < tile) pre += h[u];
+                    tot += h[u];
+                }
+            }
         }
         total[tid] = tot;
         base[tid] = pre;
@@ -126,12 +155,12 @@ __global__ __launch_bounds__(kAlignThreads) void align_scatter_kernel(
         }
     }
 
-    // Stable scatter of this tile's pairs.
+    // Stable scatter of this tile's pairs, 256 per round.
     const unsigned long long below = (1ull << lane) - 1ull;
-    for (int64_t r0 = start; r0 < end; r0 += blockDim.x) {
-        const int64_t i = r0 + tid;
-        int e = i < end ? ids[i] : -1;
-        if ((unsigned)e >= (unsigned)E) e = -1;
+#pragma unroll
+    for (int q = 0; q < PT; ++q) {
+        const int64_t i = start + q * kAlignThreads + tid;
+        const int e = my[q];
         const bool valid = e >= 0;
         unsigned long long same = __ballot(valid);
 #pragma unroll
@@ -161,16 +190,28 @@ __global__ __launch_bounds__(kAlignThreads) void align_scatter_kernel(
     }
 }
 
-// Entries per tile (a multiple of 256) and the resulting tile count.
-static int64_t align_tile_size(int64_t T, int32_t k) {
+// Entries per thread (tile = 256 * that): 4, 8 or 16, the smallest giving at
+// most kAlignMaxTiles tiles.
+static int align_per_thread(int64_t T, int32_t k) {
     const int64_t n = T * k;
-    int64_t t = (n + kAlignMaxTiles - 1) / kAlignMaxTiles;
-    t = (t + 255) / 256 * 256;
-    return t < kAlignMinTile ? kAlignMinTile : t;
+    for (int pt = 4; pt < 16; pt *= 2)
+        if ((n + pt * kAlignThreads - 1) / (pt * kAlignThreads) <= kAlignMaxTiles) return pt;
+    return 16;
 }
 static int64_t align_ntiles(int64_t T, int32_t k) {
-    const int64_t ts = align_tile_size(T, k);
+    const int64_t ts = (int64_t)align_per_thread(T, k) * kAlignThreads;
     return (T * k + ts - 1) / ts;
+}
+
+template <int PT>
+static void launch_align(const int32_t* ids, int64_t n, int E, int BM, int64_t cap, int64_t ntiles, int32_t* ws,
+                         int32_t* sorted_ids, int32_t* block_expert, int32_t* counts, int32_t* num_padded,
+                         hipStream_t s) {
+    if (ntiles > 1)
+        hipLaunchKernelGGL(align_hist_kernel<PT>, dim3((unsigned)ntiles), dim3(kAlignThreads), 0, s, ids, n, E, ws);
+    hipLaunchKernelGGL(align_scatter_kernel<PT>, dim3((unsigned)ntiles), dim3(kAlignThreads), 0, s, ids, n, E, BM, cap,
+                       (int)ntiles, (const int32_t*)ws, (int)(ntiles <= 1), sorted_ids, block_expert, counts,
+                       num_padded);
 }
 
 }  // namespace moe
@@ -212,14 +253,19 @@ extern "C" int moe_align_by_expert(const int32_t* topk_ids, int64_t T, int32_t k
     const int64_t cap = moe_align_capacity(T, k, E, block_m);
     const int64_t n = T * k;
     hipStream_t s = (hipStream_t)stream;
-    if (ntiles > 1) {
-        hipLaunchKernelGGL(align_hist_kernel, dim3((unsigned)ntiles), dim3(kAlignThreads), 0, s, topk_ids, n,
-                           align_tile_size(T, k), (int)E, (int32_t*)workspace);
-        int rc = check_launch("moe_align_by_expert (histogram)");
-        if (rc) return rc;
+    int32_t* ws = (int32_t*)workspace;
+    switch (align_per_thread(T, k)) {
+        case 4:
+            launch_align<4>(topk_ids, n, E, block_m, cap, ntiles, ws, sorted_ids, block_expert, expert_counts,
+                            num_padded, s);
+            break;
+        case 8:
+            launch_align<8>(topk_ids, n, E, block_m, cap, ntiles, ws, sorted_ids, block_expert, expert_counts,
+                            num_padded, s);
+            break;
+        default:
+            launch_align<16>(topk_ids, n, E, block_m, cap, ntiles, ws, sorted_ids, block_expert, expert_counts,
+                             num_padded, s);
     }
-    hipLaunchKernelGGL(align_scatter_kernel, dim3((unsigned)ntiles), dim3(kAlignThreads), 0, s, topk_ids, n,
-                       align_tile_size(T, k), (int)E, (int)block_m, cap, (int)ntiles, (const int32_t*)workspace, (int)(ntiles <= 1), sorted_ids,
-                       block_expert, expert_counts, num_padded);
-    return check_launch("moe_align_by_expert (scatter)");
+    return check_launch("moe_align_by_expert");
 }

@@ -79,6 +79,37 @@ def test_route_ties_from_given_logits(E, k, norm):
     assert np.array_equal(logits.cpu().numpy(), lg)  # logits are input only
 
 
+def test_route_special_logits_rank_order():
+    """Signed zeros tie (lower index first), -inf can be picked, NaN ranks
+    below every number and still yields a valid, distinct expert id."""
+    E, k = 128, 8
+    rng = np.random.default_rng(11)
+    lg = rng.standard_normal((6, E)).astype(np.float32) - 10.0
+    lg[0, 5], lg[0, 1] = 0.0, -0.0                    # tie between -0 and +0
+    lg[1, :] = -np.inf
+    lg[1, [7, 3]] = [1.0, 2.0]                        # then -inf picks, lowest index first
+    lg[2, :] = np.nan
+    lg[2, [100, 9, 50]] = [-np.inf, 3.0, -1.0]        # NaN last
+    lg[3, ::2] = np.nan                               # half NaN
+    lg[4, :] = 0.0                                    # all tied
+    lg[5, 10] = np.inf
+    logits = torch.from_numpy(lg).cuda()
+    ids = torch.empty((6, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((6, k), dtype=torch.float32, device="cuda")
+    moe.moe_route(None, None, None, logits, ids, w, 6, 0, E, k, True)
+    torch.cuda.synchronize()
+    got = ids.cpu().numpy()
+    for t in range(6):
+        row = lg[t].astype(np.float64)
+        nan = np.isnan(row)
+        # rank: numbers by value (descending, -0 == +0), then NaN; ties -> lower index
+        order = sorted(range(E), key=lambda e: (1, 0.0, e) if nan[e] else (0, -row[e], e))
+        assert list(got[t]) == order[:k], (t, got[t], order[:k])
+    assert list(got[0][:2]) == [1, 5]
+    assert list(got[1][:2]) == [3, 7] and list(got[1][2:]) == [0, 1, 2, 4, 5, 6]
+    assert list(got[2][:3]) == [9, 50, 100]
+
+
 # ----------------------------------------------------------------------------
 # Expert-grouped permutation
 # ----------------------------------------------------------------------------
