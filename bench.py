@@ -82,11 +82,11 @@ def measured_traffic(workload: str, kernel: str):
     return rec.get("hbm_bytes_per_launch")
 
 
-def algorithmic_work(shape, counts):
+def algorithmic_work(shape, counts, y_bytes=2):
     """Per-kernel algorithmic bytes and flops for one step (each touched
     expert's weights read once; activations, router weights and outputs read
     or written once; padding, re-reads and intermediates' round trips are
-    not counted)."""
+    not counted). ``y_bytes``: bytes per element of the stored y."""
     T, H, E, k, I = shape.T, shape.H, shape.E, shape.k, shape.I
     touched = int((counts > 0).sum())
     pairs = T * k
@@ -95,8 +95,8 @@ def algorithmic_work(shape, counts):
         "route": {"bytes": T * H * b + E * H * b + T * E * 4 + pairs * 8, "flops": 2 * T * H * E},
         "align": {"bytes": pairs * 4 * 2, "flops": 0},
         "gate_up": {"bytes": touched * 2 * I * H * b + T * H * b + pairs * I * b, "flops": 2 * pairs * 2 * I * H},
-        "down": {"bytes": touched * H * I * b + pairs * I * b + pairs * H * 4, "flops": 2 * pairs * H * I},
-        "combine": {"bytes": pairs * H * 4 + pairs * 4 + T * H * b, "flops": 2 * pairs * H},
+        "down": {"bytes": touched * H * I * b + pairs * I * b + pairs * H * y_bytes, "flops": 2 * pairs * H * I},
+        "combine": {"bytes": pairs * H * y_bytes + pairs * 4 + T * H * b, "flops": 2 * pairs * H},
         "layer": {"bytes": touched * 3 * I * H * b + E * H * b + 2 * T * H * b,
                   "flops": 2 * pairs * 3 * H * I + 2 * T * H * E},
         "touched_experts": touched,
@@ -341,7 +341,7 @@ def main():
                      for j, name in enumerate(KERNELS)}
     ms_per_step = elapsed * 1e3 / args.steps
     counts = b.expert_counts.cpu().numpy()
-    work = algorithmic_work(shape, counts)
+    work = algorithmic_work(shape, counts, b.y.element_size())
 
     bound = "hbm" if args.workload in ("decode", "tiny") else "mfma"
     if dense:

@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2
 
 #define MOE_OK 0
 #define MOE_ERR_INVALID (-1)     /* null required pointer, negative size, bad enum */
@@ -63,8 +63,12 @@ extern "C" {
 #define MOE_ERR_HIP (-3)         /* HIP launch/configuration error */
 #define MOE_ERR_WORKSPACE (-4)   /* workspace or capacity too small */
 
-#define MOE_OUT_BF16 0
-#define MOE_OUT_FP32 1
+/* Element types of the tensors whose type a call takes as an argument. */
+#define MOE_DTYPE_BF16 0
+#define MOE_DTYPE_FP32 1
+#define MOE_DTYPE_FP16 2
+#define MOE_OUT_BF16 MOE_DTYPE_BF16
+#define MOE_OUT_FP32 MOE_DTYPE_FP32
 
 /* Version of this ABI (MOE_ABI_VERSION). */
 int moe_abi_version(void);
@@ -188,32 +192,36 @@ int moe_grouped_gemm_gate_up_silu(const void* x, const void* w13, const int32_t*
  * every row r below num_padded with sorted_ids[r] = i not the sentinel and
  * e = block_expert[r / block_m]:
  *   y[i, h] = sum_c act[r, c] * w2[e, h, c]
- * accumulated and stored in fp32 (keeping y in fp32 keeps the layer's
- * error dominated by the final bf16 rounding of the output). Every one of
+ * accumulated in fp32 and stored as y_dtype: MOE_DTYPE_FP16 (IEEE half,
+ * round to nearest even: 11 significant bits, so the layer's error stays
+ * dominated by the final bf16 rounding of the output, at half the bytes of
+ * fp32; values beyond +-65504 become +-inf) or MOE_DTYPE_FP32. Every one of
  * the T*k rows of y is written exactly once; pad rows of act are never used
  * for a real row.
  *
- *   act  [cap, I] bf16, device (from moe_grouped_gemm_gate_up_silu).
- *   w2   [E, H, I] bf16, device, packed by moe_pack_weights (gated = 0);
- *        w2[e, h, c] above refers to the row-major weight.
- *   y    [T*k, H] fp32, device, output, in (token, slot) order.
+ *   act      [cap, I] bf16, device (from moe_grouped_gemm_gate_up_silu).
+ *   w2       [E, H, I] bf16, device, packed by moe_pack_weights (gated = 0);
+ *            w2[e, h, c] above refers to the row-major weight.
+ *   y        [T*k, H] fp16 or fp32, device, output, in (token, slot) order.
+ *   y_dtype  MOE_DTYPE_FP16 or MOE_DTYPE_FP32 (anything else: MOE_ERR_INVALID).
  */
 int moe_grouped_gemm_down(const void* act, const void* w2, const int32_t* sorted_ids, const int32_t* block_expert,
                           const int32_t* num_padded, int64_t T, int32_t k, int32_t H, int32_t I, int32_t E,
-                          int32_t block_m, int64_t cap, void* y, void* stream);
+                          int32_t block_m, int64_t cap, void* y, int32_t y_dtype, void* stream);
 
 /*
  * Weighted sum of the k expert outputs of each token ([MoE]: expert outputs
  * weighted by their scores and summed):
- *   out[t, h] = sum_j topk_weights[t, j] * y[t*k + j, h]   (fp32 accumulation)
+ *   out[t, h] = sum_j topk_weights[t, j] * y[t*k + j, h]   (fp32 accumulation,
+ *                                                          j = 0, 1, ... in order)
  *
- *   y             [T*k, H] fp32, device.
+ *   y             [T*k, H], device, MOE_DTYPE_FP16 or MOE_DTYPE_FP32 as y_dtype.
  *   topk_weights  [T, k] fp32, device.
  *   out           [T, H], device: bf16 (round to nearest even) when
  *                 out_dtype == MOE_OUT_BF16, fp32 when MOE_OUT_FP32.
  */
-int moe_combine(const void* y, const float* topk_weights, int64_t T, int32_t k, int32_t H, void* out,
-                int32_t out_dtype, void* stream);
+int moe_combine(const void* y, int32_t y_dtype, const float* topk_weights, int64_t T, int32_t k, int32_t H,
+                void* out, int32_t out_dtype, void* stream);
 
 /*
  * Fused residual add + RMSNorm, the step that precedes the MoE layer in a

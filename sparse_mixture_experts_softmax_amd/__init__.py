@@ -8,6 +8,9 @@ include/moe_mi355x.h). This package is the thin Python binding over it.
 from ._lib import (  # noqa: F401
     EXPORTS,
     LIB_PATH,
+    MOE_DTYPE_BF16,
+    MOE_DTYPE_FP16,
+    MOE_DTYPE_FP32,
     MOE_ERR_HIP,
     MOE_ERR_INVALID,
     MOE_ERR_UNSUPPORTED,

@@ -23,8 +23,12 @@ MOE_ERR_INVALID = -1
 MOE_ERR_UNSUPPORTED = -2
 MOE_ERR_HIP = -3
 MOE_ERR_WORKSPACE = -4
-MOE_OUT_BF16 = 0
-MOE_OUT_FP32 = 1
+MOE_DTYPE_BF16 = 0
+MOE_DTYPE_FP32 = 1
+MOE_DTYPE_FP16 = 2
+MOE_OUT_BF16 = MOE_DTYPE_BF16
+MOE_OUT_FP32 = MOE_DTYPE_FP32
+_Y_DTYPES = {torch.float16: MOE_DTYPE_FP16, torch.float32: MOE_DTYPE_FP32}
 
 EXPORTS = (
     "moe_abi_version",
@@ -71,8 +75,8 @@ def lib():
         L.moe_align_workspace_bytes.argtypes, L.moe_align_workspace_bytes.restype = [i64, i32, i32, i32], sz
         L.moe_align_by_expert.argtypes = [p, i64, i32, i32, i32, p, p, p, p, p, sz, p]
         L.moe_grouped_gemm_gate_up_silu.argtypes = [p, p, p, p, p, i64, i32, i32, i32, i32, i32, i64, p, p]
-        L.moe_grouped_gemm_down.argtypes = [p, p, p, p, p, i64, i32, i32, i32, i32, i32, i64, p, p]
-        L.moe_combine.argtypes = [p, p, i64, i32, i32, p, i32, p]
+        L.moe_grouped_gemm_down.argtypes = [p, p, p, p, p, i64, i32, i32, i32, i32, i32, i64, p, i32, p]
+        L.moe_combine.argtypes = [p, i32, p, i64, i32, i32, p, i32, p]
         L.moe_pick_block_m.argtypes, L.moe_pick_block_m.restype = [i64, i32, i32], i32
         L.moe_packed_weight_bytes.argtypes, L.moe_packed_weight_bytes.restype = [i32, i32, i32], sz
         L.moe_pack_weights.argtypes, L.moe_pack_weights.restype = [p, p, i32, i32, i32, i32, p], ctypes.c_int
@@ -193,19 +197,29 @@ def moe_grouped_gemm_gate_up_silu(x, w13, sorted_ids, block_expert, num_padded, 
                                                _dev(act, bf, "act"), _stream(stream, x)))
 
 
+def _y_dtype(y) -> int:
+    if y is None or y.dtype not in _Y_DTYPES:
+        raise TypeError("y must be a fp16 or fp32 tensor")
+    return _Y_DTYPES[y.dtype]
+
+
 def moe_grouped_gemm_down(act, w2, sorted_ids, block_expert, num_padded, T: int, k: int, H: int, I: int, E: int,
                           block_m: int, cap: int, y, stream=None):
+    """``y`` dtype (fp16 or fp32) selects the stored precision of y."""
     bf, i32 = torch.bfloat16, torch.int32
+    yd = _y_dtype(y)
     _check(lib().moe_grouped_gemm_down(_dev(act, bf, "act"), _dev(w2, bf, "w2"), _dev(sorted_ids, i32, "sorted_ids"),
                                        _dev(block_expert, i32, "block_expert"), _dev(num_padded, i32, "num_padded"),
-                                       T, k, H, I, E, block_m, cap, _dev(y, torch.float32, "y"),
+                                       T, k, H, I, E, block_m, cap, _dev(y, y.dtype, "y"), yd,
                                        _stream(stream, act)))
 
 
 def moe_combine(y, topk_weights, T: int, k: int, H: int, out, stream=None):
-    """``out`` dtype (bf16 or fp32) selects the output precision."""
+    """``y`` dtype (fp16 or fp32) is the stored y; ``out`` dtype (bf16 or
+    fp32) selects the output precision."""
     if out is None or out.dtype not in (torch.bfloat16, torch.float32):
         raise TypeError("out must be a bf16 or fp32 tensor")
     od = MOE_OUT_FP32 if out.dtype == torch.float32 else MOE_OUT_BF16
-    _check(lib().moe_combine(_dev(y, torch.float32, "y"), _dev(topk_weights, torch.float32, "topk_weights"), T, k, H,
+    yd = _y_dtype(y)
+    _check(lib().moe_combine(_dev(y, y.dtype, "y"), yd, _dev(topk_weights, torch.float32, "topk_weights"), T, k, H,
                              _dev(out, out.dtype, "out"), od, _stream(stream, y)))

@@ -2,7 +2,7 @@
 // accumulation), one launch for all experts.
 //
 //   gate/up:  act[r, c] = silu(x[t] . w13[e, c]) * (x[t] . w13[e, I + c])
-//   down:     y[i, h]   = act[r] . w2[e, h]      (y kept in fp32)
+//   down:     y[i, h]   = act[r] . w2[e, h]      (fp32 accumulation; y stored fp16 or fp32)
 //
 // with r a row of the expert-grouped permutation, i = sorted_ids[r] the flat
 // (token, slot) index, t = i / k its token and e = block_expert[r / BM] the
@@ -51,7 +51,7 @@ struct GemmCfg {
     static_assert(!GATED || NT % 2 == 0, "gated tile needs gate and up halves");
 };
 
-template <class C>
+template <class C, bool Y16>
 __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(
     const uint16_t* __restrict__ a_src, const uint16_t* __restrict__ w, const int32_t* __restrict__ sorted_ids,
     const int32_t* __restrict__ block_expert, const int32_t* __restrict__ num_padded, int k, int64_t n_pairs,
@@ -214,7 +214,7 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(
                 for (int q = 0; q < 4; ++q) {
                     const int row = wm * C::WTM + i * 16 + (lane / 16) * 4 + q;
                     const int64_t dst = row_src[row];
-                    if (dst >= 0) ((float*)out)[dst * N_out + col] = acc[i][j][q];
+                    if (dst >= 0) store_y<Y16>(out, dst * N_out + col, acc[i][j][q]);
                 }
             }
         }
@@ -265,7 +265,7 @@ struct WideCfg {
     static_assert(THREADS >= BM, "one row id per thread");
 };
 
-template <class C>
+template <class C, bool Y16>
 __global__ __launch_bounds__(C::THREADS) void grouped_gemm_wide_kernel(
     const uint16_t* __restrict__ a_src, const uint16_t* __restrict__ w, const int32_t* __restrict__ sorted_ids,
     const int32_t* __restrict__ block_expert, const int32_t* __restrict__ num_padded, int k, int64_t n_pairs,
@@ -429,13 +429,13 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_wide_kernel(
                     const int32_t ids[4] = {id4.x, id4.y, id4.z, id4.w};
 #pragma unroll
                     for (int u = 0; u < 4; ++u)
-                        if (real_row(ids[u])) ((float*)out)[(int64_t)ids[u] * N_out + col] = acc[i][t][4 * q4 + u];
+                        if (real_row(ids[u])) store_y<Y16>(out, (int64_t)ids[u] * N_out + col, acc[i][t][4 * q4 + u]);
                 }
         }
     }
 }
 
-template <class C>
+template <class C, bool Y16>
 static int launch_wide(const void* a, const void* w, const int32_t* sorted_ids, const int32_t* block_expert,
                        const int32_t* num_padded, int k, int64_t n_pairs, int K, int N_out, int64_t cap, void* out,
                        hipStream_t s, const char* what) {
@@ -446,12 +446,12 @@ static int launch_wide(const void* a, const void* w, const int32_t* sorted_ids, 
     const size_t lds = (size_t)C::STAGES * C::STAGE_BYTES;
     static bool attr_set = false;  // the dynamic LDS size exceeds the 64 KB default
     if (!attr_set) {
-        hipError_t err = hipFuncSetAttribute((const void*)grouped_gemm_wide_kernel<C>,
+        hipError_t err = hipFuncSetAttribute((const void*)grouped_gemm_wide_kernel<C, Y16>,
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (err != hipSuccess) return set_error(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(err));
         attr_set = true;
     }
-    hipLaunchKernelGGL(grouped_gemm_wide_kernel<C>, dim3((unsigned)grid), dim3(C::THREADS), lds, s,
+    hipLaunchKernelGGL((grouped_gemm_wide_kernel<C, Y16>), dim3((unsigned)grid), dim3(C::THREADS), lds, s,
                        (const uint16_t*)a, (const uint16_t*)w, sorted_ids, block_expert, num_padded, k, n_pairs, K,
                        N_out, n_tiles, out);
     return check_launch(what);
@@ -465,7 +465,7 @@ static int launch_wide(const void* a, const void* w, const int32_t* sorted_ids, 
 // HBM straight into MFMA B-fragments, 1 KB contiguous per load, U k-steps per
 // stage, two stages in flight. The gathered activation rows (A-fragments) are re-read from L2
 // (the activation matrix is small in this regime).
-template <bool GATED, int NW, int NTILE, int U>
+template <bool GATED, int NW, int NTILE, int U, bool Y16>
 __global__ __launch_bounds__(NW* kWave) void grouped_gemm_skinny_kernel(
     const uint16_t* __restrict__ a_src, const uint16_t* __restrict__ w, const int32_t* __restrict__ sorted_ids,
     const int32_t* __restrict__ block_expert, const int32_t* __restrict__ num_padded, int k, int64_t n_pairs,
@@ -564,13 +564,13 @@ __global__ __launch_bounds__(NW* kWave) void grouped_gemm_skinny_kernel(
 #pragma unroll
             for (int j = 0; j < NTILE; ++j) {
                 const int col = c0 + j * 16 + r16;
-                if (col < N_out) ((float*)out)[(int64_t)dst * N_out + col] = acc[j][q];
+                if (col < N_out) store_y<Y16>(out, (int64_t)dst * N_out + col, acc[j][q]);
             }
         }
     }
 }
 
-template <bool GATED, int NW, int NTILE, int U>
+template <bool GATED, int NW, int NTILE, int U, bool Y16>
 static int launch_skinny_cfg(const void* a, const void* w, const int32_t* sorted_ids, const int32_t* block_expert,
                              const int32_t* num_padded, int k, int64_t n_pairs, int K, int N_out, int64_t cap,
                              void* out, hipStream_t s, const char* what) {
@@ -578,26 +578,26 @@ static int launch_skinny_cfg(const void* a, const void* w, const int32_t* sorted
     const int n_tiles = (N_out + cols_per_wg - 1) / cols_per_wg;
     const int64_t grid = (cap / 16) * n_tiles;
     if (grid >= ((int64_t)1 << 31)) return set_error(MOE_ERR_UNSUPPORTED, "%s: grid too large", what);
-    hipLaunchKernelGGL((grouped_gemm_skinny_kernel<GATED, NW, NTILE, U>), dim3((unsigned)grid), dim3(NW * kWave), 0,
+    hipLaunchKernelGGL((grouped_gemm_skinny_kernel<GATED, NW, NTILE, U, Y16>), dim3((unsigned)grid), dim3(NW * kWave), 0,
                        s, (const uint16_t*)a, (const uint16_t*)w, sorted_ids, block_expert, num_padded, k, n_pairs, K,
                        N_out, n_tiles, out);
     return check_launch(what);
 }
 
-template <bool GATED>
+template <bool GATED, bool Y16>
 static int launch_skinny(const void* a, const void* w, const int32_t* sorted_ids, const int32_t* block_expert,
                          const int32_t* num_padded, int k, int64_t n_pairs, int K, int N_out, int64_t cap, void* out,
                          hipStream_t s, const char* what) {
     // Chosen by sweeps on the decode-shaped layer: single-wave workgroups
     // (finest load balance) for gate/up; the down shape is insensitive.
     if (GATED)
-        return launch_skinny_cfg<true, 1, 2, 8>(a, w, sorted_ids, block_expert, num_padded, k, n_pairs, K, N_out, cap,
+        return launch_skinny_cfg<true, 1, 2, 8, false>(a, w, sorted_ids, block_expert, num_padded, k, n_pairs, K, N_out, cap,
                                                 out, s, what);
-    return launch_skinny_cfg<false, 4, 4, 4>(a, w, sorted_ids, block_expert, num_padded, k, n_pairs, K, N_out, cap,
+    return launch_skinny_cfg<false, 4, 4, 4, Y16>(a, w, sorted_ids, block_expert, num_padded, k, n_pairs, K, N_out, cap,
                                              out, s, what);
 }
 
-template <class C>
+template <class C, bool Y16>
 static int launch_gemm(const void* a, const void* w, const int32_t* sorted_ids, const int32_t* block_expert,
                        const int32_t* num_padded, int k, int64_t n_pairs, int K, int N_out, int64_t cap, void* out,
                        hipStream_t s, const char* what) {
@@ -606,28 +606,28 @@ static int launch_gemm(const void* a, const void* w, const int32_t* sorted_ids, 
     const int64_t m_blocks = cap / C::BM;
     const int64_t grid = m_blocks * n_tiles;
     if (grid >= ((int64_t)1 << 31)) return set_error(MOE_ERR_UNSUPPORTED, "%s: grid too large", what);
-    hipLaunchKernelGGL(grouped_gemm_kernel<C>, dim3((unsigned)grid), dim3(C::THREADS), 0, s, (const uint16_t*)a,
+    hipLaunchKernelGGL((grouped_gemm_kernel<C, Y16>), dim3((unsigned)grid), dim3(C::THREADS), 0, s, (const uint16_t*)a,
                        (const uint16_t*)w, sorted_ids, block_expert, num_padded, k, n_pairs, K, N_out, n_tiles,
                        out);
     return check_launch(what);
 }
 
-template <bool GATED>
+template <bool GATED, bool Y16>
 static int dispatch_gemm(int32_t block_m, const void* a, const void* w, const int32_t* sorted_ids,
                          const int32_t* block_expert, const int32_t* num_padded, int k, int64_t n_pairs, int K,
                          int N_out, int64_t cap, void* out, hipStream_t s, const char* what) {
     switch (block_m) {
         case 16:
-            return launch_skinny<GATED>(a, w, sorted_ids, block_expert, num_padded, k, n_pairs, K, N_out, cap, out, s,
+            return launch_skinny<GATED, Y16>(a, w, sorted_ids, block_expert, num_padded, k, n_pairs, K, N_out, cap, out, s,
                                         what);
         case 32:
-            return launch_gemm<GemmCfg<32, 128, GATED>>(a, w, sorted_ids, block_expert, num_padded, k, n_pairs, K,
+            return launch_gemm<GemmCfg<32, 128, GATED>, Y16>(a, w, sorted_ids, block_expert, num_padded, k, n_pairs, K,
                                                        N_out, cap, out, s, what);
         case 64:
-            return launch_wide<WideCfg<GATED, 64, 4>>(a, w, sorted_ids, block_expert, num_padded, k, n_pairs, K,
+            return launch_wide<WideCfg<GATED, 64, 4>, Y16>(a, w, sorted_ids, block_expert, num_padded, k, n_pairs, K,
                                                       N_out, cap, out, s, what);
         case 128:
-            return launch_wide<WideCfg<GATED, 128, 3>>(a, w, sorted_ids, block_expert, num_padded, k, n_pairs, K,
+            return launch_wide<WideCfg<GATED, 128, 3>, Y16>(a, w, sorted_ids, block_expert, num_padded, k, n_pairs, K,
                                                        N_out, cap, out, s, what);
     }
     return set_error(MOE_ERR_UNSUPPORTED, "%s: block_m=%d not in {16,32,64,128}", what, block_m);
@@ -663,21 +663,26 @@ extern "C" int moe_grouped_gemm_gate_up_silu(const void* x, const void* w13, con
     const char* fn = "moe_grouped_gemm_gate_up_silu";
     int rc = check_gemm_args(fn, x, w13, sorted_ids, block_expert, num_padded, T, k, H, I, E, block_m, cap, act);
     if (rc || T == 0) return rc;
-    return dispatch_gemm<true>(block_m, x, w13, sorted_ids, block_expert, num_padded, k, T * k, H, I, cap, act,
-                               (hipStream_t)stream, fn);
+    return dispatch_gemm<true, false>(block_m, x, w13, sorted_ids, block_expert, num_padded, k, T * k, H, I, cap,
+                                      act, (hipStream_t)stream, fn);
 }
 
 extern "C" int moe_grouped_gemm_down(const void* act, const void* w2, const int32_t* sorted_ids,
                                      const int32_t* block_expert, const int32_t* num_padded, int64_t T, int32_t k,
                                      int32_t H, int32_t I, int32_t E, int32_t block_m, int64_t cap, void* y,
-                                     void* stream) {
+                                     int32_t y_dtype, void* stream) {
     using namespace moe;
     clear_error();
     const char* fn = "moe_grouped_gemm_down";
+    if (y_dtype != MOE_DTYPE_FP16 && y_dtype != MOE_DTYPE_FP32)
+        return set_error(MOE_ERR_INVALID, "%s: y_dtype=%d is neither fp16 (2) nor fp32 (1)", fn, y_dtype);
     int rc = check_gemm_args(fn, act, w2, sorted_ids, block_expert, num_padded, T, k, H, I, E, block_m, cap, y);
     if (rc || T == 0) return rc;
-    return dispatch_gemm<false>(block_m, act, w2, sorted_ids, block_expert, num_padded, k, T * k, I, H, cap, y,
-                                (hipStream_t)stream, fn);
+    if (y_dtype == MOE_DTYPE_FP16)
+        return dispatch_gemm<false, true>(block_m, act, w2, sorted_ids, block_expert, num_padded, k, T * k, I, H, cap,
+                                          y, (hipStream_t)stream, fn);
+    return dispatch_gemm<false, false>(block_m, act, w2, sorted_ids, block_expert, num_padded, k, T * k, I, H, cap, y,
+                                       (hipStream_t)stream, fn);
 }
 
 extern "C" int32_t moe_pick_block_m(int64_t T, int32_t k, int32_t E) {

@@ -79,6 +79,16 @@ __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// One element of the down projection's output: fp16 (round to nearest even)
+// when Y16, else fp32.
+template <bool Y16>
+__device__ __forceinline__ void store_y(void* y, int64_t idx, float v) {
+    if constexpr (Y16)
+        ((_Float16*)y)[idx] = (_Float16)v;
+    else
+        ((float*)y)[idx] = v;
+}
+
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
 
 template <typename T>

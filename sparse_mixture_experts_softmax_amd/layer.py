@@ -75,7 +75,9 @@ class MoEBuffers:
 
 
 def allocate(T: int, H: int, E: int, k: int, I: int, device, block_m: Optional[int] = None,
-             out_dtype=torch.bfloat16) -> MoEBuffers:
+             out_dtype=torch.bfloat16, y_dtype=torch.float16) -> MoEBuffers:
+    """Buffers of one layer call. ``y_dtype`` (fp16 or fp32) is the stored
+    precision of the expert outputs between the down GEMM and the combine."""
     if block_m is None:
         block_m = _lib.moe_pick_block_m(T, k, E)
     cap = _lib.moe_align_capacity(T, k, E, block_m)
@@ -93,7 +95,7 @@ def allocate(T: int, H: int, E: int, k: int, I: int, device, block_m: Optional[i
         num_padded=torch.empty((1,), **i32),
         workspace=torch.empty((ws_bytes,), dtype=torch.uint8, device=device) if ws_bytes else None,
         act=torch.empty((cap, I), dtype=torch.bfloat16, device=device),
-        y=torch.empty((T * k, H), dtype=torch.float32, device=device),
+        y=torch.empty((T * k, H), dtype=y_dtype, device=device),
         out=torch.empty((T, H), dtype=out_dtype, device=device),
         block_m=block_m,
         cap=cap,
@@ -103,14 +105,16 @@ def allocate(T: int, H: int, E: int, k: int, I: int, device, block_m: Optional[i
 def moe_layer(x: torch.Tensor, w_router: torch.Tensor, w13: Optional[torch.Tensor] = None,
               w2: Optional[torch.Tensor] = None, *, top_k: int, norm_topk_prob: bool = True,
               router_bias: Optional[torch.Tensor] = None, packed: Optional[PackedExperts] = None,
-              block_m: Optional[int] = None, out_dtype=torch.bfloat16, buffers: Optional[MoEBuffers] = None,
-              stream=None) -> torch.Tensor:
+              block_m: Optional[int] = None, out_dtype=torch.bfloat16, y_dtype=torch.float16,
+              buffers: Optional[MoEBuffers] = None, stream=None) -> torch.Tensor:
     """out[T, H] = sparse MoE layer of x[T, H] (no residual).
 
     x [T, H], w_router [E, H]: bf16 on the GPU; router_bias [E] fp32 or None.
     Expert weights either as ``packed`` (from pack_experts, the fast path)
     or as row-major w13 [E, 2I, H] (gate rows, then up rows) and w2 [E, H, I],
-    which are then packed on every call."""
+    which are then packed on every call. ``y_dtype`` (fp16 or fp32) is the
+    stored precision of the expert outputs (ignored when ``buffers`` is
+    given: its y decides)."""
     if packed is None:
         if w13 is None or w2 is None:
             raise ValueError("pass packed=pack_experts(w13, w2) or the row-major w13 and w2")
@@ -129,7 +133,7 @@ def moe_layer(x: torch.Tensor, w_router: torch.Tensor, w13: Optional[torch.Tenso
                          f"experts E={packed.num_experts} H={packed.hidden_size} I={I}")
     w13p, w2p = packed.w13, packed.w2
     k = int(top_k)
-    b = buffers if buffers is not None else allocate(T, H, E, k, I, x.device, block_m, out_dtype)
+    b = buffers if buffers is not None else allocate(T, H, E, k, I, x.device, block_m, out_dtype, y_dtype)
     s = _lib._stream(stream, x)
     _lib.moe_route(x, w_router, router_bias, b.logits, b.topk_ids, b.topk_weights, T, H, E, k, norm_topk_prob, s)
     _lib.moe_align_by_expert(b.topk_ids, T, k, E, b.block_m, b.sorted_ids, b.block_expert, b.expert_counts,
@@ -143,7 +147,7 @@ def moe_layer(x: torch.Tensor, w_router: torch.Tensor, w13: Optional[torch.Tenso
 
 
 def gated_mlp(x: torch.Tensor, packed: PackedExperts, *, block_m: Optional[int] = None, out_dtype=torch.bfloat16,
-              stream=None) -> torch.Tensor:
+              y_dtype=torch.float16, stream=None) -> torch.Tensor:
     """Dense SwiGLU GatedMLP (down(silu(gate(x)) * up(x)), the "Models and
     weight loading" page's GatedMLP) through the same grouped GEMMs: every
     token is routed to the single expert of ``packed`` (num_experts == 1)
@@ -155,7 +159,7 @@ def gated_mlp(x: torch.Tensor, packed: PackedExperts, *, block_m: Optional[int] 
         raise ValueError(f"x must be [T, {packed.hidden_size}]")
     T, H = x.shape
     I = packed.intermediate_size
-    b = allocate(T, H, 1, 1, I, x.device, block_m, out_dtype)
+    b = allocate(T, H, 1, 1, I, x.device, block_m, out_dtype, y_dtype)
     s = _lib._stream(stream, x)
     ids = torch.zeros((T, 1), dtype=torch.int32, device=x.device)
     ones = torch.ones((T, 1), dtype=torch.float32, device=x.device)

@@ -69,11 +69,11 @@ def device_inputs(inp, key=None):
     return d
 
 
-def run_layer(inp, dev=None, block_m=None, out_dtype=torch.bfloat16):
+def run_layer(inp, dev=None, block_m=None, out_dtype=torch.bfloat16, y_dtype=torch.float16):
     """The layer through the C ABI; returns (out, buffers)."""
     s = inp.shape
     dev = dev or device_inputs(inp)
-    bufs = moe.allocate(s.T, s.H, s.E, s.k, s.I, "cuda", block_m, out_dtype)
+    bufs = moe.allocate(s.T, s.H, s.E, s.k, s.I, "cuda", block_m, out_dtype, y_dtype)
     out = moe.moe_layer(dev["x"], dev["w_router"], top_k=s.k, packed=dev["packed"],
                         norm_topk_prob=s.norm_topk_prob, router_bias=dev["bias"], buffers=bufs)
     torch.cuda.synchronize()

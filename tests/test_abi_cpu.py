@@ -28,7 +28,7 @@ def test_library_exports_every_declared_symbol():
     for name in names:
         assert hasattr(L, name), f"{name} declared in the header but not exported"
     assert set(names) == set(_lib.EXPORTS)
-    assert moe.moe_abi_version() == 1
+    assert moe.moe_abi_version() == 2
 
 
 def test_capacity_and_workspace():
@@ -89,7 +89,10 @@ def test_align_validation():
 
 def test_gemm_validation():
     L = _raw()
-    for fn in (L.moe_grouped_gemm_gate_up_silu, L.moe_grouped_gemm_down):
+    F16 = _lib.MOE_DTYPE_FP16
+    calls = (lambda *a: L.moe_grouped_gemm_gate_up_silu(*a[:-1], NULL),
+             lambda *a: L.moe_grouped_gemm_down(*a[:-1], F16, NULL))
+    for fn in calls:
         # (a, w, sorted, blk, npad, T, k, H, I, E, block_m, cap, out, stream)
         cap = moe.moe_align_capacity(16, 2, 8, 16)
         assert fn(FAKE, FAKE, FAKE, FAKE, FAKE, 16, 2, 64, 48, 8, 16, cap, FAKE, NULL) == _lib.MOE_ERR_UNSUPPORTED
@@ -100,6 +103,12 @@ def test_gemm_validation():
         misaligned = ctypes.c_void_p(0x1002)
         assert fn(misaligned, FAKE, FAKE, FAKE, FAKE, 16, 2, 64, 32, 8, 16, cap, FAKE, NULL) == _lib.MOE_ERR_INVALID
         assert fn(NULL, NULL, NULL, NULL, NULL, 0, 2, 64, 32, 8, 16, 0, NULL, NULL) == _lib.MOE_OK
+    # y is fp16 or fp32, nothing else (bf16 included)
+    cap = moe.moe_align_capacity(16, 2, 8, 16)
+    for bad in (_lib.MOE_DTYPE_BF16, 3, -1):
+        assert L.moe_grouped_gemm_down(FAKE, FAKE, FAKE, FAKE, FAKE, 16, 2, 64, 32, 8, 16, cap, FAKE, bad,
+                                       NULL) == _lib.MOE_ERR_INVALID
+        assert "y_dtype" in moe.moe_last_error()
 
 
 def test_pack_validation():
@@ -128,11 +137,14 @@ def test_rmsnorm_validation():
 
 def test_combine_validation():
     L = _raw()
-    assert L.moe_combine(FAKE, FAKE, 4, 2, 64, FAKE, 7, NULL) == _lib.MOE_ERR_INVALID
-    assert L.moe_combine(FAKE, FAKE, 4, 33, 64, FAKE, 0, NULL) == _lib.MOE_ERR_UNSUPPORTED
-    assert L.moe_combine(FAKE, FAKE, 4, 2, 32, FAKE, 0, NULL) == _lib.MOE_ERR_UNSUPPORTED
-    assert L.moe_combine(NULL, FAKE, 4, 2, 64, FAKE, 0, NULL) == _lib.MOE_ERR_INVALID
-    assert L.moe_combine(NULL, NULL, 0, 2, 64, NULL, 0, NULL) == _lib.MOE_OK
+    F16, F32 = _lib.MOE_DTYPE_FP16, _lib.MOE_DTYPE_FP32
+    assert L.moe_combine(FAKE, F16, FAKE, 4, 2, 64, FAKE, 7, NULL) == _lib.MOE_ERR_INVALID
+    assert L.moe_combine(FAKE, _lib.MOE_DTYPE_BF16, FAKE, 4, 2, 64, FAKE, 0, NULL) == _lib.MOE_ERR_INVALID
+    assert "y_dtype" in moe.moe_last_error()
+    assert L.moe_combine(FAKE, F16, FAKE, 4, 33, 64, FAKE, 0, NULL) == _lib.MOE_ERR_UNSUPPORTED
+    assert L.moe_combine(FAKE, F32, FAKE, 4, 2, 32, FAKE, 0, NULL) == _lib.MOE_ERR_UNSUPPORTED
+    assert L.moe_combine(NULL, F16, FAKE, 4, 2, 64, FAKE, 0, NULL) == _lib.MOE_ERR_INVALID
+    assert L.moe_combine(NULL, F32, NULL, 0, 2, 64, NULL, 0, NULL) == _lib.MOE_OK
 
 
 def test_python_binding_rejects_host_tensors_and_wrong_dtypes():

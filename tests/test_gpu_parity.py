@@ -182,13 +182,18 @@ def test_pack_weights_matches_layout_definition(E, N, K, gated):
 # ----------------------------------------------------------------------------
 # Each kernel against the oracle step it implements
 # ----------------------------------------------------------------------------
-@pytest.mark.parametrize("name", ["tiny", "decode", "prefill", "large"])
-def test_gemms_and_combine_against_oracle_steps(name):
-    log(f"steps {name}")
+F16, F32 = torch.float16, torch.float32
+
+
+@pytest.mark.parametrize("name,y_dtype", [("tiny", F16), ("tiny", F32), ("decode", F16), ("decode", F32),
+                                          ("prefill", F16), ("prefill", F32), ("large", F16)])
+def test_gemms_and_combine_against_oracle_steps(name, y_dtype):
+    log(f"steps {name} y {y_dtype}")
     inp = host_inputs(name)
     s = inp.shape
     dev = device_inputs(inp, key=name)
-    out, b = run_layer(inp, dev)
+    out, b = run_layer(inp, dev, y_dtype=y_dtype)
+    assert b.y.dtype == y_dtype
     sorted_ids = b.sorted_ids.cpu().numpy()
     block_expert = b.block_expert.cpu().numpy()
     npad = int(b.num_padded.item())
@@ -213,8 +218,11 @@ def test_gemms_and_combine_against_oracle_steps(name):
         y_ref.append(oracle.expert_down(a_gpu, inp.w2[e])[0])
         y_gpu.append(_f64(b.y[i]))
     elem_close(np.array(act_gpu), np.array(act_ref), what="gate_up act")
-    # y is fp32: only fp32 accumulation error (far below the floor)
-    elem_close(np.array(y_gpu), np.array(y_ref), rel=1e-5, floor_frac=1e-4, what="down y")
+    # fp32 accumulation error (far below the floor), plus the rounding of the
+    # stored y: half an fp16 ulp (2^-11 relative; fp16 subnormals, below
+    # 6.1e-5, are far below the floor)
+    rel = 1e-5 + (2.0 ** -11 if y_dtype == F16 else 0.0)
+    elem_close(np.array(y_gpu), np.array(y_ref), rel=rel, floor_frac=1e-4, what="down y")
     # combine: fp32 output against the oracle's weighted sum of the GPU's y
     toks = sample_tokens(s.T, 128)
     out32 = torch.empty((s.T, s.H), dtype=torch.float32, device="cuda")
@@ -231,13 +239,13 @@ def test_gemms_and_combine_against_oracle_steps(name):
 # ----------------------------------------------------------------------------
 # The whole layer
 # ----------------------------------------------------------------------------
-@pytest.mark.parametrize("name", CONFIG_NAMES)
-def test_layer_matches_oracle(name):
-    log(f"layer {name}")
+@pytest.mark.parametrize("name,y_dtype", [(n, F16) for n in CONFIG_NAMES] + [("tiny", F32), ("large", F32)])
+def test_layer_matches_oracle(name, y_dtype):
+    log(f"layer {name} y {y_dtype}")
     inp = host_inputs(name)
     s = inp.shape
     dev = device_inputs(inp, key=name)
-    out, b = run_layer(inp, dev)
+    out, b = run_layer(inp, dev, y_dtype=y_dtype)
     toks = sample_tokens(s.T, 96)
     ref, ref_ids, ref_w = oracle.moe_layer(inp.x, inp.w_router, inp.w13, inp.w2, s.k, s.norm_topk_prob,
                                            inp.router_bias, toks)
