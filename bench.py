@@ -113,7 +113,7 @@ def cpu_baseline(inp, seconds: float):
 
     s = inp.shape
     orc = oracle.default()
-    n = min(s.T, 8)
+    n = min(s.T, 2 * orc.max_threads())  # enough tokens to occupy every thread once the estimate is scaled up
     t0 = time.perf_counter()
     orc.moe_layer(inp.x, inp.w_router, inp.w13, inp.w2, s.k, s.norm_topk_prob, inp.router_bias, np.arange(n))
     per_token = (time.perf_counter() - t0) / n
