@@ -350,6 +350,15 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_wide_kernel(
 #pragma unroll
         for (int t = 0; t < C::TN; ++t) acc[i][t] = f32x16{};
 
+    // The real rows of a block are a prefix (a block belongs to one expert,
+    // whose pad rows follow its real ones), so a 32-row accumulator tile whose
+    // first row is a pad row holds only pad rows: its fragment reads and
+    // MFMAs are skipped (its accumulators stay zero, which is what the
+    // epilogue writes for pad rows anyway). n_live is wave-uniform.
+    static_assert(C::TM == 2, "two 32-row accumulator tiles per wave");
+    const int n_live = (real_row(__builtin_amdgcn_readfirstlane(ids_blk[wm * 64])) ? 1 : 0) +
+                       (real_row(__builtin_amdgcn_readfirstlane(ids_blk[wm * 64 + 32])) ? 1 : 0);
+
 #pragma unroll
     for (int p = 0; p < S - 1; ++p)
         if (p < nkt) issue(p);
@@ -364,6 +373,7 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_wide_kernel(
         __builtin_amdgcn_s_barrier();
         if (kt + S - 1 < nkt) issue(kt + S - 1);
         const char* stage = smem + (kt % S) * C::STAGE_BYTES;
+        if (n_live == 0) continue;
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
             u32x4 fa[C::TM], fb[C::TN];
@@ -371,7 +381,7 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_wide_kernel(
 #pragma unroll
             for (int i = 0; i < C::TM; ++i) {
                 const int r = wm * 64 + i * 32 + lane % 32;
-                fa[i] = *(const u32x4*)(stage + r * 64 + ((chunk ^ ((r >> 2) & 3)) * 16));
+                if (i < n_live) fa[i] = *(const u32x4*)(stage + r * 64 + ((chunk ^ ((r >> 2) & 3)) * 16));
             }
 #pragma unroll
             for (int t = 0; t < C::TN; ++t) {
@@ -380,8 +390,10 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_wide_kernel(
             }
 #pragma unroll
             for (int i = 0; i < C::TM; ++i)
+                if (i < n_live) {
 #pragma unroll
-                for (int t = 0; t < C::TN; ++t) acc[i][t] = mfma32x32x16(fa[i], fb[t], acc[i][t]);
+                    for (int t = 0; t < C::TN; ++t) acc[i][t] = mfma32x32x16(fa[i], fb[t], acc[i][t]);
+                }
         }
     }
 
