@@ -85,6 +85,118 @@ __global__ __launch_bounds__(kRouteSlices* kWave) void router_logits_kernel(cons
     }
 }
 
+// Large batches: a workgroup covers 64 tokens (one 16-token MFMA tile per
+// wave) x 16*ET experts, so the router weight is read once per 64 tokens
+// instead of once per 16. Both operands go global -> LDS by direct copies
+// (global_load_lds_dwordx4, lane l of a copy lands at base + 16*l, i.e. as
+// an MFMA fragment), in chunks of RC k-steps through a ring of NB chunk
+// buffers with NB-1 chunks in flight: the router fragments of a chunk are
+// copied once and read by all four waves, each wave copies its own
+// activation fragments. The sums follow router_logits_kernel exactly: H is
+// cut into the same four slices, each slice accumulated k-step by k-step
+// into its own accumulator, the four slice sums added in order, then the
+// bias; a token's logits are the same bits whichever kernel and batch size
+// computed them. Needs the slice length (H/32/4 k-steps) to be a multiple
+// of RC.
+constexpr int kRouteWideTokens = 64;
+constexpr int kRouteChunk = 4;  // k-steps per chunk (RC)
+
+template <int ET, int NB_>
+struct RouteWide {
+    static constexpr int RC = kRouteChunk, NB = NB_, D = NB - 1;
+    static constexpr int W_COPIES = ET * RC / kRouteSlices;  // router fragments per wave per chunk
+    static constexpr int X_COPIES = RC;                      // activation fragments per wave per chunk
+    static constexpr int OPS = W_COPIES + X_COPIES;
+    static constexpr int W_BYTES = ET * RC * 1024;
+    static constexpr int X_BYTES = kRouteSlices * RC * 1024;
+    static constexpr int CHUNK_BYTES = W_BYTES + X_BYTES;
+    static_assert((ET * RC) % kRouteSlices == 0, "router fragments split evenly over the waves");
+    static_assert(OPS * (D - 1) < 64, "vmcnt range");
+    static_assert(NB * CHUNK_BYTES <= 160 * 1024, "LDS");
+};
+
+template <int ET, int NB_>
+__global__ __launch_bounds__(kRouteSlices* kWave) void router_logits_wide_kernel(const uint16_t* __restrict__ x,
+                                                                                 const uint16_t* __restrict__ wr,
+                                                                                 const float* __restrict__ bias,
+                                                                                 float* __restrict__ logits,
+                                                                                 int64_t T, int H, int E) {
+    using C = RouteWide<ET, NB_>;
+    constexpr int RC = C::RC, NB = C::NB, D = C::D;
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    const int64_t t0 = (int64_t)blockIdx.x * kRouteWideTokens + wave * kRouteTokens;
+    const int e0 = blockIdx.y * 16 * ET;
+    const int row = lane % 16, koff = (lane / 16) * 8;
+    // unconditional copies from clamped rows: rows past T are never stored,
+    // experts past E only feed logits that are never stored
+    const uint16_t* xsrc = x + min(t0 + row, T - 1) * (int64_t)H + koff;
+    const uint16_t* wsrc[C::W_COPIES];
+    int wdst[C::W_COPIES];
+#pragma unroll
+    for (int j = 0; j < C::W_COPIES; ++j) {
+        const int f = wave * C::W_COPIES + j;  // fragment (expert tile f / RC, k-step f % RC)
+        wsrc[j] = wr + (int64_t)min(e0 + 16 * (f / RC) + row, E - 1) * H + (f % RC) * 32 + koff;
+        wdst[j] = f * 1024;
+    }
+    const int ksteps = H / 32, per = ksteps / kRouteSlices, nchunk = ksteps / RC;
+    auto issue = [&](int c) {
+        char* buf = smem + (c % NB) * C::CHUNK_BYTES;
+#pragma unroll
+        for (int j = 0; j < C::W_COPIES; ++j) lds_dma16(wsrc[j] + c * RC * 32, buf + wdst[j]);
+#pragma unroll
+        for (int s = 0; s < RC; ++s) lds_dma16(xsrc + (c * RC + s) * 32, buf + C::W_BYTES + (wave * RC + s) * 1024);
+    };
+    f32x4 acc[kRouteSlices][ET];
+#pragma unroll
+    for (int sl = 0; sl < kRouteSlices; ++sl)
+#pragma unroll
+        for (int j = 0; j < ET; ++j) acc[sl][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    for (int c = 0; c < D && c < nchunk; ++c) issue(c);
+    int c = 0;
+#pragma unroll
+    for (int sl = 0; sl < kRouteSlices; ++sl) {
+        for (int cc = 0; cc < per / RC; ++cc, ++c) {
+            // this wave's copies of chunk c are done once at most the ops of
+            // the later chunks already issued remain; the barrier publishes
+            // the chunk and frees the buffer of chunk c - 1
+            const int later = min(D - 1, nchunk - 1 - c);
+            static_assert(D <= 5, "wait ladder covers up to four later chunks");
+            if (later >= 4) vm_wait<4 * C::OPS>();
+            else if (later == 3) vm_wait<3 * C::OPS>();
+            else if (later == 2) vm_wait<2 * C::OPS>();
+            else if (later == 1) vm_wait<C::OPS>();
+            else vm_wait<0>();
+            __builtin_amdgcn_s_barrier();
+            if (c + D < nchunk) issue(c + D);
+            const char* buf = smem + (c % NB) * C::CHUNK_BYTES;
+#pragma unroll
+            for (int s = 0; s < RC; ++s) {
+                const u32x4 a = *(const u32x4*)(buf + C::W_BYTES + (wave * RC + s) * 1024 + lane * 16);
+#pragma unroll
+                for (int j = 0; j < ET; ++j)
+                    acc[sl][j] = mfma16x16x32(a, *(const u32x4*)(buf + (j * RC + s) * 1024 + lane * 16), acc[sl][j]);
+            }
+        }
+    }
+    // D layout: lane holds rows 4*(lane/16)+i, column lane%16 of each tile
+#pragma unroll
+    for (int j = 0; j < ET; ++j) {
+        const int e = e0 + 16 * j + lane % 16;
+        const float b = (bias && e < E) ? bias[e] : 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int64_t t = t0 + (lane / 16) * 4 + i;
+            float v = acc[0][j][i];
+#pragma unroll
+            for (int sl = 1; sl < kRouteSlices; ++sl) v += acc[sl][j][i];
+            if (bias) v += b;
+            if (t < T && e < E) logits[t * E + e] = v;
+        }
+    }
+}
+
 // Wave-wide reductions without LDS traffic: DPP lane permutations inside
 // each row of 16 lanes (xor 1, xor 2, mirror within 8, mirror within 16)
 // leave every lane holding its row's result; the four row results are then
@@ -209,6 +321,22 @@ __global__ __launch_bounds__(kTopkWaves* kWave) void route_topk_kernel(const flo
     }
 }
 
+template <int NB>
+static int launch_route_wide(dim3 grid, const void* x, const void* w_router, const float* bias, float* logits,
+                             int64_t T, int32_t H, int32_t E, hipStream_t s) {
+    constexpr int lds = RouteWide<2, NB>::NB * RouteWide<2, NB>::CHUNK_BYTES;
+    static bool attr_set = false;  // the dynamic LDS size exceeds the 64 KB default
+    if (!attr_set) {
+        hipError_t err = hipFuncSetAttribute((const void*)router_logits_wide_kernel<2, NB>,
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+        if (err != hipSuccess) return set_error(MOE_ERR_HIP, "moe_route: %s", hipGetErrorString(err));
+        attr_set = true;
+    }
+    hipLaunchKernelGGL((router_logits_wide_kernel<2, NB>), grid, dim3(kRouteSlices * kWave), lds, s,
+                       (const uint16_t*)x, (const uint16_t*)w_router, bias, logits, T, (int)H, (int)E);
+    return MOE_OK;
+}
+
 }  // namespace moe
 
 extern "C" int moe_route(const void* x, const void* w_router, const float* router_bias, float* logits,
@@ -237,7 +365,16 @@ extern "C" int moe_route(const void* x, const void* w_router, const float* route
         const int64_t tblocks = (T + kRouteTokens - 1) / kRouteTokens;
         const int ntiles = (E + 15) / 16;
         if (tblocks >= ((int64_t)1 << 31)) return set_error(MOE_ERR_UNSUPPORTED, "moe_route: T too large");
-        if (T <= 256 || ntiles < 8) {
+        const int ksteps = H / 32;
+        if (T > 256 && ksteps % (kRouteSlices * kRouteChunk) == 0) {
+            // one round of workgroups on the 256 CUs: the deepest ring (one
+            // workgroup per CU); more: a shallower ring, two per CU
+            const dim3 grid((unsigned)((T + kRouteWideTokens - 1) / kRouteWideTokens), (unsigned)((ntiles + 1) / 2));
+            const int rc = (int64_t)grid.x * grid.y <= 256
+                               ? launch_route_wide<6>(grid, x, w_router, router_bias, logits, T, H, E, s)
+                               : launch_route_wide<3>(grid, x, w_router, router_bias, logits, T, H, E, s);
+            if (rc) return rc;
+        } else if (T <= 256 || ntiles < 8) {
             hipLaunchKernelGGL(router_logits_kernel<1>, dim3((unsigned)tblocks, (unsigned)ntiles),
                                dim3(kRouteSlices * kWave), 0, s, (const uint16_t*)x, (const uint16_t*)w_router,
                                router_bias, logits, T, (int)H, (int)E);

@@ -79,6 +79,29 @@ def test_route_ties_from_given_logits(E, k, norm):
     assert np.array_equal(logits.cpu().numpy(), lg)  # logits are input only
 
 
+@pytest.mark.parametrize("T,H,E", [(333, 512, 40), (1000, 2048, 128), (300, 4096, 256), (17000, 512, 32)])
+def test_router_logits_same_bits_for_small_and_large_batches(T, H, E):
+    """Batches above 256 tokens take the workgroup-shared router kernel; a
+    token's logits must not depend on which kernel (batch size) computed
+    them, and both must match the oracle."""
+    inp = custom_inputs(f"router{T}", T, H, E, min(8, E), 64, seed=T + H)
+    dev = device_inputs(inp)
+
+    def route(n):
+        lg = torch.empty((n, E), dtype=torch.float32, device="cuda")
+        ids = torch.empty((n, min(8, E)), dtype=torch.int32, device="cuda")
+        w = torch.empty((n, min(8, E)), dtype=torch.float32, device="cuda")
+        moe.moe_route(dev["x"][:n].contiguous(), dev["w_router"], dev["bias"], lg, ids, w, n, H, E, min(8, E), True)
+        torch.cuda.synchronize()
+        return lg.cpu().numpy()
+
+    big, small = route(T), route(200)
+    assert np.array_equal(big[:200].view(np.uint32), small.view(np.uint32))
+    toks = sample_tokens(T, 64)
+    ref = oracle.router_logits(inp.x[toks], inp.w_router, inp.router_bias)
+    assert (np.abs(big[toks] - ref) <= logits_bound(inp, toks)).all()
+
+
 def test_route_special_logits_rank_order():
     """Signed zeros tie (lower index first), -inf can be picked, NaN ranks
     below every number and still yields a valid, distinct expert id."""
