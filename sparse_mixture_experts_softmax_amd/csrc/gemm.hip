@@ -263,6 +263,9 @@ struct WideCfg {
     static_assert(STAGES >= 2 && STAGES <= 5, "stages");
     static_assert(STAGES * STAGE_BYTES <= 160 * 1024, "LDS");
     static_assert(THREADS >= BM, "one row id per thread");
+    // the epilogue reuses the stages: 1 KB of row ids, then the bf16 act tile
+    // or a 32-row pass of the fp32 y tile
+    static_assert(1024 + (GATED ? BM * COLS * 2 : 32 * COLS * 4) <= STAGES * STAGE_BYTES, "epilogue staging");
 };
 
 template <class C, bool Y16>
@@ -398,19 +401,24 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_wide_kernel(
     }
 
     // The stages are free once every wave is done with the last one: they
-    // now hold the block's row ids.
+    // now hold the block's row ids (first 1 KB) and the output tile, staged
+    // so that every global store writes whole rows, 16 bytes per lane (the
+    // accumulator layout gives each lane one column, so direct stores would
+    // write 2- or 4-byte pieces).
     __syncthreads();
     int32_t* ids_s = (int32_t*)smem;
+    char* stile = smem + 1024;
     if (tid < BM) ids_s[tid] = my_id;
     __syncthreads();
 
-    // Epilogue: element q of a 32x32 tile is row 8*(q/4) + 4*(lane/32) + q%4,
-    // column lane%32; the ids of rows q..q+3 come as one 16-byte LDS read.
+    // Element q of a 32x32 accumulator tile is row 8*(q/4) + 4*(lane/32) +
+    // q%4, column lane%32; the ids of rows q..q+3 come as one 16-byte read.
     if (C::GATED) {
+        // the whole BM x COLS bf16 tile at once
+        uint16_t* st = (uint16_t*)stile;
 #pragma unroll
         for (int g = 0; g < C::TN / 2; ++g) {
-            const int col = tn * C::COLS + wn * (C::WTN / 2) + g * 32 + lane % 32;
-            if (col >= N_out) continue;
+            const int col = wn * (C::WTN / 2) + g * 32 + lane % 32;
 #pragma unroll
             for (int i = 0; i < C::TM; ++i)
 #pragma unroll
@@ -422,27 +430,56 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_wide_kernel(
                     for (int u = 0; u < 4; ++u) {
                         const int q = 4 * q4 + u;
                         const float v = silu(acc[i][g][q]) * acc[i][g + C::TN / 2][q];
-                        ((uint16_t*)out)[((int64_t)mb * BM + row0 + u) * N_out + col] =
-                            f32_to_bf16(real_row(ids[u]) ? v : 0.f);
+                        st[(row0 + u) * C::COLS + col] = f32_to_bf16(real_row(ids[u]) ? v : 0.f);
                     }
                 }
         }
+        __syncthreads();
+        // a row is COLS * 2 bytes = 32 lanes x 16 bytes: two rows per instruction
+        constexpr int CPR = C::COLS * 2 / 16;
+        static_assert(kWave % CPR == 0, "whole rows per wave instruction");
+        constexpr int RPI = kWave / CPR;
+        const int cidx = lane % CPR, col = tn * C::COLS + cidx * 8;
+        for (int r = wave * RPI + lane / CPR; r < BM; r += C::THREADS / kWave * RPI) {
+            const u32x4 v = *(const u32x4*)(stile + (r * CPR + cidx) * 16);
+            if (col < N_out) *(u32x4*)((uint16_t*)out + ((int64_t)mb * BM + r) * N_out + col) = v;
+        }
     } else {
+        // 32-row passes (one accumulator tile row of the waves of one wm)
+        constexpr int ES = Y16 ? 2 : 4;
+        constexpr int CPR = C::COLS * ES / 16;  // 16-byte chunks per row
+        static_assert(CPR % kWave == 0, "a row is whole wave instructions");
 #pragma unroll
-        for (int t = 0; t < C::TN; ++t) {
-            const int col = tn * C::COLS + wn * C::WTN + t * 32 + lane % 32;
-            if (col >= N_out) continue;
+        for (int pass = 0; pass < BM / 32; ++pass) {
+            const int pm = pass / C::TM, pi = pass % C::TM;
+            if (wm == pm) {
 #pragma unroll
-            for (int i = 0; i < C::TM; ++i)
+                for (int t = 0; t < C::TN; ++t) {
+                    const int col = wn * C::WTN + t * 32 + lane % 32;
 #pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4) {
-                    const int row0 = wm * 64 + i * 32 + 8 * q4 + 4 * (lane / 32);
-                    const int4 id4 = *(const int4*)&ids_s[row0];
-                    const int32_t ids[4] = {id4.x, id4.y, id4.z, id4.w};
-#pragma unroll
-                    for (int u = 0; u < 4; ++u)
-                        if (real_row(ids[u])) store_y<Y16>(out, (int64_t)ids[u] * N_out + col, acc[i][t][4 * q4 + u]);
+                    for (int q = 0; q < 16; ++q) {
+                        const int row = 8 * (q / 4) + 4 * (lane / 32) + q % 4;
+                        const float v = acc[pi][t][q];
+                        if constexpr (Y16)
+                            ((_Float16*)stile)[row * C::COLS + col] = (_Float16)v;
+                        else
+                            ((float*)stile)[row * C::COLS + col] = v;
+                    }
                 }
+            }
+            __syncthreads();
+            for (int r = wave; r < 32; r += C::THREADS / kWave) {
+                const int32_t id = ids_s[pass * 32 + r];
+                if (!real_row(id)) continue;
+#pragma unroll
+                for (int c = 0; c < CPR / kWave; ++c) {
+                    const int cidx = c * kWave + lane;
+                    const int col = tn * C::COLS + cidx * (16 / ES);
+                    const u32x4 v = *(const u32x4*)(stile + (r * CPR + cidx) * 16);
+                    if (col < N_out) *(u32x4*)((char*)out + ((int64_t)id * N_out + col) * ES) = v;
+                }
+            }
+            __syncthreads();
         }
     }
 }
