@@ -435,20 +435,17 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_wide_kernel(
                 }
         }
         __syncthreads();
-        // a row is COLS * 2 bytes = 32 lanes x 16 bytes: two rows per instruction
-        constexpr int CPR = C::COLS * 2 / 16;
-        static_assert(kWave % CPR == 0, "whole rows per wave instruction");
-        constexpr int RPI = kWave / CPR;
-        const int cidx = lane % CPR, col = tn * C::COLS + cidx * 8;
-        for (int r = wave * RPI + lane / CPR; r < BM; r += C::THREADS / kWave * RPI) {
-            const u32x4 v = *(const u32x4*)(stile + (r * CPR + cidx) * 16);
+        // consecutive threads store consecutive 16-byte chunks of a row
+        constexpr int CPR = C::COLS * 2 / 16;  // chunks per row
+        for (int ci = tid; ci < BM * CPR; ci += C::THREADS) {
+            const int r = ci / CPR, col = tn * C::COLS + (ci % CPR) * 8;
+            const u32x4 v = *(const u32x4*)(stile + ci * 16);
             if (col < N_out) *(u32x4*)((uint16_t*)out + ((int64_t)mb * BM + r) * N_out + col) = v;
         }
     } else {
         // 32-row passes (one accumulator tile row of the waves of one wm)
         constexpr int ES = Y16 ? 2 : 4;
         constexpr int CPR = C::COLS * ES / 16;  // 16-byte chunks per row
-        static_assert(CPR % kWave == 0, "a row is whole wave instructions");
 #pragma unroll
         for (int pass = 0; pass < BM / 32; ++pass) {
             const int pm = pass / C::TM, pi = pass % C::TM;
@@ -468,16 +465,11 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_wide_kernel(
                 }
             }
             __syncthreads();
-            for (int r = wave; r < 32; r += C::THREADS / kWave) {
+            for (int ci = tid; ci < 32 * CPR; ci += C::THREADS) {
+                const int r = ci / CPR, col = tn * C::COLS + (ci % CPR) * (16 / ES);
                 const int32_t id = ids_s[pass * 32 + r];
-                if (!real_row(id)) continue;
-#pragma unroll
-                for (int c = 0; c < CPR / kWave; ++c) {
-                    const int cidx = c * kWave + lane;
-                    const int col = tn * C::COLS + cidx * (16 / ES);
-                    const u32x4 v = *(const u32x4*)(stile + (r * CPR + cidx) * 16);
-                    if (col < N_out) *(u32x4*)((char*)out + ((int64_t)id * N_out + col) * ES) = v;
-                }
+                const u32x4 v = *(const u32x4*)(stile + ci * 16);
+                if (real_row(id) && col < N_out) *(u32x4*)((char*)out + ((int64_t)id * N_out + col) * ES) = v;
             }
             __syncthreads();
         }
