@@ -24,6 +24,18 @@ int check_launch(const char* what) {
     return MOE_OK;
 }
 
+int ensure_dynamic_lds(const void* kernel, int bytes, std::atomic<uint64_t>& done, const char* what) {
+    int dev = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess) return set_error(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(err));
+    const uint64_t bit = 1ull << (dev & 63);
+    if (done.load(std::memory_order_acquire) & bit) return MOE_OK;
+    err = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (err != hipSuccess) return set_error(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(err));
+    done.fetch_or(bit, std::memory_order_release);
+    return MOE_OK;
+}
+
 bool valid_block_m(int32_t block_m) { return block_m == 16 || block_m == 32 || block_m == 64 || block_m == 128; }
 
 int check_shape(const char* fn, int64_t T, int32_t H, int32_t E, int32_t k, int32_t I) {

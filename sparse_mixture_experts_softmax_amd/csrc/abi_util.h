@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "moe_mi355x.h"
 
 namespace moe {
@@ -18,6 +20,11 @@ int check_launch(const char* what);
 
 constexpr int kMaxExperts = 256;
 constexpr int kMaxTopK = 32;
+
+// Raises `kernel`'s dynamic LDS limit to `bytes` (HIP's default is 64 KB)
+// once per device; `done` is the call site's mask of devices already set
+// (thread-safe: a race only repeats the idempotent attribute call).
+int ensure_dynamic_lds(const void* kernel, int bytes, std::atomic<uint64_t>& done, const char* what);
 
 // Shared limits on (T, H, E, k, I); I < 0 means "not used by this call".
 int check_shape(const char* fn, int64_t T, int32_t H, int32_t E, int32_t k, int32_t I);

@@ -1,4 +1,4 @@
-// Grouped expert GEMMs on the matrix cores (v_mfma_f32_16x16x32_bf16, fp32
+// Grouped expert GEMMs on the matrix cores (bf16 operands, fp32
 // accumulation), one launch for all experts.
 //
 //   gate/up:  act[r, c] = silu(x[t] . w13[e, c]) * (x[t] . w13[e, I + c])
@@ -11,10 +11,15 @@
 // each a contiguous 1 KB MFMA B operand; gate and up bands interleaved), so
 // every weight load instruction reads 1 KB contiguous.
 //
-// Grid: one workgroup per (row block, N tile), row-block major; blocks past
-// num_padded (read on the device) return at once, so no host sync is needed.
+// Three kernels, chosen by the row-block size block_m:
+//   16       grouped_gemm_skinny_kernel (weight streaming, decode-sized)
+//   32       grouped_gemm_kernel        (16x16x32 MFMA, LDS-staged)
+//   64, 128  grouped_gemm_wide_kernel   (32x32x16 MFMA, direct-to-LDS copies)
+// Grids cover one workgroup per (row block, N tile) of the capacity; blocks
+// past num_padded (read on the device) return at once, so no host sync is
+// needed.
 //
-// General kernel (row blocks of 32..128): each workgroup stages BMxBK
+// General kernel (row blocks of 32): each workgroup stages BMxBK
 // activation rows (gathered through sorted_ids for gate/up) in padded
 // row-major LDS and the tile's BN/16 weight bands (BK/32 fragments each) in
 // fragment-major LDS, double-buffered: the next K tile is loaded into
@@ -238,13 +243,14 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(
 // waves and frees the oldest one for the next copy.
 //
 // Tiles are ordered so each XCD (workgroups go to the 8 XCDs round robin)
-// takes a contiguous share of the real (row block, N tile) pairs, N-tile
-// major and row block minor: the row blocks of one expert run together on one
-// XCD and share its L2 for the weight tile.
-template <bool GATED_, int BM_, int STAGES_, bool MB_MAJOR_ = true>
+// takes a contiguous share of the real (row block, N tile) pairs, row-block
+// major: the row blocks of one expert run together on one XCD and share its
+// L2 for the weight tile. 32-row accumulator tiles that hold only pad rows
+// skip their MFMAs; the epilogue stages the output tile in LDS and stores
+// whole rows.
+template <bool GATED_, int BM_, int STAGES_>
 struct WideCfg {
     static constexpr bool GATED = GATED_;
-    static constexpr bool MB_MAJOR = MB_MAJOR_;  // tile order inside an XCD's share
     static constexpr int BM = BM_;
     static constexpr int WAVES_M = BM / 64;
     static constexpr int WAVES_N = 4;
@@ -283,8 +289,8 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_wide_kernel(
     const int64_t share = (real + 7) / 8;
     const int64_t logical = (int64_t)(blockIdx.x % 8) * share + blockIdx.x / 8;
     if ((int64_t)(blockIdx.x / 8) >= share || logical >= real) return;
-    const int tn = C::MB_MAJOR ? (int)(logical % n_tiles) : (int)(logical / m_real);
-    const int mb = C::MB_MAJOR ? (int)(logical / n_tiles) : (int)(logical % m_real);
+    const int tn = (int)(logical % n_tiles);
+    const int mb = (int)(logical / n_tiles);
     const int e = block_expert[mb];
     if (e < 0) return;
     const int64_t w_rows = C::GATED ? 2 * (int64_t)N_out : (int64_t)N_out;
@@ -485,13 +491,9 @@ static int launch_wide(const void* a, const void* w, const int32_t* sorted_ids, 
     grid = (grid + 7) / 8 * 8;
     if (grid >= ((int64_t)1 << 31)) return set_error(MOE_ERR_UNSUPPORTED, "%s: grid too large", what);
     const size_t lds = (size_t)C::STAGES * C::STAGE_BYTES;
-    static bool attr_set = false;  // the dynamic LDS size exceeds the 64 KB default
-    if (!attr_set) {
-        hipError_t err = hipFuncSetAttribute((const void*)grouped_gemm_wide_kernel<C, Y16>,
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (err != hipSuccess) return set_error(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(err));
-        attr_set = true;
-    }
+    static std::atomic<uint64_t> lds_set{0};
+    const int rc = ensure_dynamic_lds((const void*)grouped_gemm_wide_kernel<C, Y16>, (int)lds, lds_set, what);
+    if (rc) return rc;
     hipLaunchKernelGGL((grouped_gemm_wide_kernel<C, Y16>), dim3((unsigned)grid), dim3(C::THREADS), lds, s,
                        (const uint16_t*)a, (const uint16_t*)w, sorted_ids, block_expert, num_padded, k, n_pairs, K,
                        N_out, n_tiles, out);

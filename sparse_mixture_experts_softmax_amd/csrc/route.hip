@@ -325,13 +325,9 @@ template <int NB>
 static int launch_route_wide(dim3 grid, const void* x, const void* w_router, const float* bias, float* logits,
                              int64_t T, int32_t H, int32_t E, hipStream_t s) {
     constexpr int lds = RouteWide<2, NB>::NB * RouteWide<2, NB>::CHUNK_BYTES;
-    static bool attr_set = false;  // the dynamic LDS size exceeds the 64 KB default
-    if (!attr_set) {
-        hipError_t err = hipFuncSetAttribute((const void*)router_logits_wide_kernel<2, NB>,
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-        if (err != hipSuccess) return set_error(MOE_ERR_HIP, "moe_route: %s", hipGetErrorString(err));
-        attr_set = true;
-    }
+    static std::atomic<uint64_t> lds_set{0};
+    const int rc = ensure_dynamic_lds((const void*)router_logits_wide_kernel<2, NB>, lds, lds_set, "moe_route");
+    if (rc) return rc;
     hipLaunchKernelGGL((router_logits_wide_kernel<2, NB>), grid, dim3(kRouteSlices * kWave), lds, s,
                        (const uint16_t*)x, (const uint16_t*)w_router, bias, logits, T, (int)H, (int)E);
     return MOE_OK;
