@@ -160,3 +160,11 @@ def test_python_binding_rejects_host_tensors_and_wrong_dtypes():
 def test_status_raises_with_message():
     with pytest.raises(moe.MoEError, match="E=300"):
         _lib._check(_raw().moe_route(FAKE, FAKE, NULL, FAKE, FAKE, FAKE, 4, 64, 300, 2, 1, NULL))
+
+
+def test_header_abi_version_matches_library():
+    """build() checks the loaded library against the header's version."""
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    with open(os.path.join(root, "include", "moe_mi355x.h")) as fh:
+        header_version = int(re.search(r"#define MOE_ABI_VERSION (\d+)", fh.read()).group(1))
+    assert moe.moe_abi_version() == header_version
