@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 2
+#define MOE_ABI_VERSION 3
 
 #define MOE_OK 0
 #define MOE_ERR_INVALID (-1)     /* null required pointer, negative size, bad enum */
@@ -180,7 +180,12 @@ int moe_pack_weights(const void* w, void* w_packed, int32_t E, int32_t N, int32_
  *              weight.
  *   sorted_ids, block_expert, num_padded: from moe_align_by_expert with the
  *              same T, k, E, block_m; cap = moe_align_capacity(...).
- *   act        [cap, I] bf16, device, output (rows in sorted order).
+ *   act        [cap, I] bf16, device, output: rows in sorted order, stored
+ *              as MFMA fragment blocks like the packed weights (16-row x
+ *              32-column blocks of 512 elements, row-band major; element
+ *              (r, c) at ((r/16)*(I/32) + c/32)*512 + (16*((c%32)/8) + r%16)*8
+ *              + c%8), so the down projection reads 1 KB blocks. Rows below
+ *              num_padded occupy the first num_padded*I elements.
  */
 int moe_grouped_gemm_gate_up_silu(const void* x, const void* w13, const int32_t* sorted_ids,
                                   const int32_t* block_expert, const int32_t* num_padded, int64_t T, int32_t k,
@@ -199,7 +204,8 @@ int moe_grouped_gemm_gate_up_silu(const void* x, const void* w13, const int32_t*
  * the T*k rows of y is written exactly once; pad rows of act are never used
  * for a real row.
  *
- *   act      [cap, I] bf16, device (from moe_grouped_gemm_gate_up_silu).
+ *   act      [cap, I] bf16, device, in the fragment-block layout written by
+ *            moe_grouped_gemm_gate_up_silu.
  *   w2       [E, H, I] bf16, device, packed by moe_pack_weights (gated = 0);
  *            w2[e, h, c] above refers to the row-major weight.
  *   y        [T*k, H] fp16 or fp32, device, output, in (token, slot) order.

@@ -99,7 +99,7 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(
             a_ok[j] = a_ok[j] && src >= 0;
             a_ptr[j] = a_src + (src >= 0 ? src : 0) + kc;
         } else {
-            a_ptr[j] = a_src + ((int64_t)mb * BM + (a_ok[j] ? row : 0)) * K + kc;
+            a_ptr[j] = a_src + frag_index((int64_t)mb * BM + (a_ok[j] ? row : 0), kc, K);
         }
     }
     // B chunk c of a K tile: band-in-tile c / (KS*64), k-step (c / 64) % KS,
@@ -125,7 +125,8 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(
         for (int j = 0; j < C::A_PER_T; ++j) {
             const int kc = ((tid + j * C::THREADS) % (BK / 8)) * 8;
             const bool in = k0 + kc < K;
-            ra[j] = sel(a_ok[j] && in, ld16(a_ptr[j] + (in ? k0 : 0)));
+            // act fragments: columns k0.. of a row sit k0 / 32 blocks of 512 on
+            ra[j] = sel(a_ok[j] && in, ld16(a_ptr[j] + (in ? (C::GATED ? k0 : k0 * 16) : 0)));
         }
 #pragma unroll
         for (int j = 0; j < C::B_PER_T; ++j) {
@@ -204,7 +205,7 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(
                 for (int q = 0; q < 4; ++q) {
                     const int row = wm * C::WTM + i * 16 + (lane / 16) * 4 + q;
                     const float v = silu(acc[i][g][q]) * acc[i][g + HALF_NT][q];
-                    ((uint16_t*)out)[((int64_t)mb * BM + row) * N_out + col] = f32_to_bf16(v);
+                    ((uint16_t*)out)[frag_index((int64_t)mb * BM + row, col, N_out)] = f32_to_bf16(v);
                 }
             }
         }
@@ -308,16 +309,17 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_wide_kernel(
     for (int j = 0; j < C::COPIES_PER_WAVE; ++j) {
         const int q = wave * C::COPIES_PER_WAVE + j;
         if (q < BM / 16) {
-            const int row = q * 16 + lane / 4;
-            const int chunk = (lane % 4) ^ ((row >> 2) & 3);  // LDS slot lane%4 holds this chunk
-            int64_t base;
             if (C::GATED) {
+                // 16 gathered x rows, 64 bytes each
+                const int row = q * 16 + lane / 4;
+                const int chunk = (lane % 4) ^ ((row >> 2) & 3);  // LDS slot lane%4 holds this chunk
                 const int32_t id = ids_blk[row];
-                base = real_row(id) ? (int64_t)(id / k) * K : 0;  // sentinel rows: any valid row
+                const int64_t base = real_row(id) ? (int64_t)(id / k) * K : 0;  // sentinel rows: any valid row
+                src[j] = a_src + base + chunk * 8;
             } else {
-                base = ((int64_t)mb * BM + row) * K;
+                // one 1 KB act fragment block (16 rows x 32 columns)
+                src[j] = a_src + (int64_t)(mb * (BM / 16) + q) * (K / 32) * 512 + lane * 8;
             }
-            src[j] = a_src + base + chunk * 8;
             dst[j] = q * 1024;
         } else {
             const int bt = q - BM / 16;
@@ -332,7 +334,8 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_wide_kernel(
 #pragma unroll
         for (int j = 0; j < C::COPIES_PER_WAVE; ++j) {
             const int q = wave * C::COPIES_PER_WAVE + j;
-            const int64_t step = q < BM / 16 ? 32 : 512;  // A: 32 columns; B: one packed block
+            // gathered rows: 32 columns on; fragment blocks: the next block
+            const int64_t step = (q < BM / 16 && C::GATED) ? 32 : 512;
             lds_dma16(src[j] + kt * step, stage + dst[j]);
         }
     };
@@ -390,7 +393,10 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_wide_kernel(
 #pragma unroll
             for (int i = 0; i < C::TM; ++i) {
                 const int r = wm * 64 + i * 32 + lane % 32;
-                if (i < n_live) fa[i] = *(const u32x4*)(stage + r * 64 + ((chunk ^ ((r >> 2) & 3)) * 16));
+                // gathered rows: swizzled row-major; act: fragment blocks
+                const int off = C::GATED ? r * 64 + ((chunk ^ ((r >> 2) & 3)) * 16)
+                                         : (r / 16) * 1024 + (chunk * 16 + r % 16) * 16;
+                if (i < n_live) fa[i] = *(const u32x4*)(stage + off);
             }
 #pragma unroll
             for (int t = 0; t < C::TN; ++t) {
@@ -420,7 +426,9 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_wide_kernel(
     // Element q of a 32x32 accumulator tile is row 8*(q/4) + 4*(lane/32) +
     // q%4, column lane%32; the ids of rows q..q+3 come as one 16-byte read.
     if (C::GATED) {
-        // the whole BM x COLS bf16 tile at once
+        // the whole BM x COLS bf16 tile at once, row-major with the 16-byte
+        // chunks of row r XOR-swizzled by r%16 (the packed read-out below
+        // gathers 16 rows at one column: without it they share a bank)
         uint16_t* st = (uint16_t*)stile;
 #pragma unroll
         for (int g = 0; g < C::TN / 2; ++g) {
@@ -436,17 +444,27 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_wide_kernel(
                     for (int u = 0; u < 4; ++u) {
                         const int q = 4 * q4 + u;
                         const float v = silu(acc[i][g][q]) * acc[i][g + C::TN / 2][q];
-                        st[(row0 + u) * C::COLS + col] = f32_to_bf16(real_row(ids[u]) ? v : 0.f);
+                        const int r = row0 + u;
+                        st[r * C::COLS + (((col >> 3) ^ (r & 15)) << 3) + (col & 7)] =
+                            f32_to_bf16(real_row(ids[u]) ? v : 0.f);
                     }
                 }
         }
         __syncthreads();
-        // consecutive threads store consecutive 16-byte chunks of a row
-        constexpr int CPR = C::COLS * 2 / 16;  // chunks per row
-        for (int ci = tid; ci < BM * CPR; ci += C::THREADS) {
-            const int r = ci / CPR, col = tn * C::COLS + (ci % CPR) * 8;
-            const u32x4 v = *(const u32x4*)(stile + ci * 16);
-            if (col < N_out) *(u32x4*)((uint16_t*)out + ((int64_t)mb * BM + r) * N_out + col) = v;
+        // act is stored as fragment blocks (16 rows x 32 columns, 1 KB):
+        // consecutive threads write consecutive 16-byte lanes of a block
+        constexpr int CPR = C::COLS * 2 / 16;  // 16-byte chunks per staged row
+        constexpr int KB = C::COLS / 32;       // column blocks per tile
+        static_assert(CPR >= 16, "the chunk swizzle needs 16 chunks per row");
+        for (int ci = tid; ci < (BM / 16) * KB * kWave; ci += C::THREADS) {
+            const int blk = ci / kWave, l = ci % kWave;
+            const int band = blk / KB, kb = blk % KB;
+            const int r = band * 16 + l % 16, chunk = kb * 4 + l / 16;
+            const int col = tn * C::COLS + kb * 32;
+            const u32x4 v = *(const u32x4*)(stile + (r * CPR + (chunk ^ (r & 15))) * 16);
+            if (col < N_out)
+                *(u32x4*)((uint16_t*)out +
+                          ((int64_t)(mb * (BM / 16) + band) * (N_out / 32) + col / 32) * 512 + l * 8) = v;
         }
     } else {
         // 32-row passes (one accumulator tile row of the waves of one wm)
@@ -530,9 +548,12 @@ __global__ __launch_bounds__(NW* kWave) void grouped_gemm_skinny_kernel(
     // A: row r16 of the block
     const int32_t id = sorted_ids[(int64_t)mb * BM + r16];
     const bool a_ok = id >= 0 && (int64_t)id < n_pairs;
+    // gate/up: gathered x rows (a k-step is 32 columns on); down: the row
+    // block's act fragments (a k-step is the next 512-element block)
     const uint16_t* ap;
     if (GATED) ap = a_src + (a_ok ? (int64_t)(id / k) * K : 0) + koff;  // sentinel -> row 0, zeroed
-    else ap = a_src + ((int64_t)mb * BM + r16) * K + koff;
+    else ap = a_src + (int64_t)mb * (K / 32) * 512 + lane * 8;
+    constexpr int A_STEP = GATED ? 32 : 512;
     const bool a_live = GATED ? a_ok : true;
 
     // B: NTILE packed bands of 16 weight rows (gate/up: gate band 2c, up
@@ -558,8 +579,7 @@ __global__ __launch_bounds__(NW* kWave) void grouped_gemm_skinny_kernel(
     auto load = [&](int st, int s0) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int kk = (s0 + u) * 32;
-            ra[st][u] = sel(a_live, ld16(ap + kk));
+            ra[st][u] = sel(a_live, ld16(ap + (s0 + u) * A_STEP));
 #pragma unroll
             for (int j = 0; j < NTILE; ++j) rb[st][j][u] = ld16(bp[j] + (s0 + u) * 512);
         }
@@ -580,7 +600,7 @@ __global__ __launch_bounds__(NW* kWave) void grouped_gemm_skinny_kernel(
         if (c + 1 < nstage) compute(1);
     }
     for (int s = nstage * U; s < ksteps; ++s) {
-        const u32x4 a = sel(a_live, ld16(ap + s * 32));
+        const u32x4 a = sel(a_live, ld16(ap + s * A_STEP));
 #pragma unroll
         for (int j = 0; j < NTILE; ++j) acc[j] = mfma16x16x32(a, ld16(bp[j] + s * 512), acc[j]);
     }
@@ -595,7 +615,7 @@ __global__ __launch_bounds__(NW* kWave) void grouped_gemm_skinny_kernel(
             for (int q = 0; q < 4; ++q) {
                 const int row = (lane / 16) * 4 + q;
                 const float v = silu(acc[g][q]) * acc[g + NTILE / 2][q];
-                ((uint16_t*)out)[((int64_t)mb * BM + row) * N_out + col] = f32_to_bf16(v);
+                ((uint16_t*)out)[frag_index((int64_t)mb * BM + row, col, N_out)] = f32_to_bf16(v);
             }
         }
     } else {

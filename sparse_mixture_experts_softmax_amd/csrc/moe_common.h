@@ -79,6 +79,16 @@ __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// Index of element (r, c) of a bf16 matrix with `cols` columns (a multiple
+// of 32) stored as MFMA fragment blocks, the layout of moe_pack_weights and
+// of act: 16-row x 32-column blocks of 512 elements, row-band major, column
+// block minor; inside a block lane l = 16*((c%32)/8) + r%16 holds columns
+// 8*((c%32)/8) .. +7 of row r, so one 16-byte lane load is one lane of an
+// MFMA operand fragment.
+__device__ __forceinline__ int64_t frag_index(int64_t r, int c, int cols) {
+    return ((r >> 4) * (cols >> 5) + (c >> 5)) * 512 + ((((c & 31) >> 3) << 4) + (r & 15)) * 8 + (c & 7);
+}
+
 // One element of the down projection's output: fp16 (round to nearest even)
 // when Y16, else fp32.
 template <bool Y16>

@@ -96,6 +96,20 @@ def pack_reference(w: np.ndarray, gated: bool) -> np.ndarray:
     return np.ascontiguousarray(b.transpose(0, 1, 3, 4, 2, 5)).reshape(E, N, K)
 
 
+def act_rows(act: torch.Tensor) -> torch.Tensor:
+    """Row-major [cap, I] view of act, which the GEMMs store as fragment
+    blocks (16 rows x 32 columns per block, lane l holding row l%16 at
+    columns 8*(l//16)..; the layout of the packed weights)."""
+    cap, I = act.shape
+    return act.reshape(cap // 16, I // 32, 4, 16, 8).permute(0, 3, 1, 2, 4).reshape(cap, I)
+
+
+def act_blocks(rows: torch.Tensor) -> torch.Tensor:
+    """Inverse of act_rows: row-major rows to the fragment-block layout."""
+    cap, I = rows.shape
+    return rows.reshape(cap // 16, 16, I // 32, 4, 8).permute(0, 2, 3, 1, 4).reshape(cap, I).contiguous()
+
+
 def sample_tokens(T: int, n: int, seed: int = 0) -> np.ndarray:
     """First, last and ragged-tail tokens plus a seeded random sample."""
     if T <= n:

@@ -28,7 +28,7 @@ def test_library_exports_every_declared_symbol():
     for name in names:
         assert hasattr(L, name), f"{name} declared in the header but not exported"
     assert set(names) == set(_lib.EXPORTS)
-    assert moe.moe_abi_version() == 2
+    assert moe.moe_abi_version() == 3
 
 
 def test_capacity_and_workspace():

@@ -13,8 +13,8 @@ import torch
 import oracle
 import synth
 import sparse_mixture_experts_softmax_amd as moe
-from gpu_cases import (CONFIG_NAMES, bf16_tensor, custom_inputs, device_inputs, host_inputs, layer_tolerance, log,
-                       logits_bound, pack_reference, run_layer, sample_tokens, to_bits)
+from gpu_cases import (CONFIG_NAMES, act_blocks, act_rows, bf16_tensor, custom_inputs, device_inputs, host_inputs,
+                       layer_tolerance, log, logits_bound, pack_reference, run_layer, sample_tokens, to_bits)
 
 pytestmark = pytest.mark.gpu
 
@@ -226,7 +226,7 @@ def test_gemms_and_combine_against_oracle_steps(name, y_dtype):
     rng = np.random.default_rng(0)
     if rows.size > 192:
         rows = np.sort(rng.choice(rows, 192, replace=False))
-    act = b.act
+    act = act_rows(b.act)
     # pad rows of act are zero
     if pads.size:
         assert not _f64(act[torch.from_numpy(pads).cuda()]).any()
@@ -335,7 +335,9 @@ def test_nan_poison_unused_experts_and_pad_rows():
     # poison pad rows of act between the two GEMMs
     n = s.T * s.k
     pad = torch.from_numpy(np.nonzero(b.sorted_ids.cpu().numpy() == n)[0]).cuda()
-    b.act[pad] = float("nan")
+    rows = act_rows(b.act).clone()
+    rows[pad] = float("nan")
+    b.act.copy_(act_blocks(rows))
     moe.moe_grouped_gemm_down(b.act, dev["packed"].w2, b.sorted_ids, b.block_expert, b.num_padded, s.T, s.k, s.H,
                               s.I, s.E, b.block_m, b.cap, b.y)
     out2 = torch.empty_like(out)
