@@ -235,20 +235,20 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(
 // with (BM/64) x 4 waves.
 //
 // Operands reach LDS by direct global->LDS copies (global_load_lds_dwordx4,
-// no registers), S stages deep: stage kt holds the activation rows' columns
-// [32kt, 32kt+32) and one packed 1 KB block per weight band. The A rows are
-// stored 64 bytes apart with their four 16-byte chunks XOR-swizzled by
-// (row/4)%4 so that fragment reads are free of bank conflicts; B blocks are
-// stored as packed. Each wave waits only for its own copies of the stage it
+// no registers), S stages deep (128-row blocks: 4 for gate/up, all 160 KB of
+// LDS; 3 for down, where a fourth stage measured no faster): stage kt holds
+// the activation rows' columns [32kt, 32kt+32) and one packed 1 KB block per
+// weight band. The A rows are stored 64 bytes apart with their four 16-byte
+// chunks XOR-swizzled by (row/4)%4 so that fragment reads are free of bank
+// conflicts; B blocks are stored as packed. Each wave waits only for its own copies of the stage it
 // needs (explicit vmcnt), then a bare s_barrier publishes the stage to all
 // waves and frees the oldest one for the next copy.
 //
 // Tiles are ordered so each XCD (workgroups go to the 8 XCDs round robin)
 // takes a contiguous share of the real (row block, N tile) pairs, row-block
 // major: the row blocks of one expert run together on one XCD and share its
-// L2 for the weight tile. 32-row accumulator tiles that hold only pad rows
-// skip their MFMAs; the epilogue stages the output tile in LDS and stores
-// whole rows.
+// L2 for the weight tile. The epilogue stages the output tile in LDS and
+// stores whole rows.
 template <bool GATED_, int BM_, int STAGES_>
 struct WideCfg {
     static constexpr bool GATED = GATED_;
@@ -362,33 +362,17 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_wide_kernel(
 #pragma unroll
         for (int t = 0; t < C::TN; ++t) acc[i][t] = f32x16{};
 
-    // The real rows of a block are a prefix (a block belongs to one expert,
-    // whose pad rows follow its real ones), so a 32-row accumulator tile whose
-    // first row is a pad row holds only pad rows: its fragment reads and
-    // MFMAs are skipped (its accumulators stay zero, which is what the
-    // epilogue writes for pad rows anyway). n_live is wave-uniform.
-    static_assert(C::TM == 2, "two 32-row accumulator tiles per wave");
-    const int n_live = (real_row(__builtin_amdgcn_readfirstlane(ids_blk[wm * 64])) ? 1 : 0) +
-                       (real_row(__builtin_amdgcn_readfirstlane(ids_blk[wm * 64 + 32])) ? 1 : 0);
-
-#pragma unroll
-    for (int p = 0; p < S - 1; ++p)
-        if (p < nkt) issue(p);
-    for (int kt = 0; kt < nkt; ++kt) {
-        // wait for this wave's copies of stage kt (the copies of up to S-2
-        // later stages may still be in flight), then publish it
-        const int later = min(S - 2, nkt - 1 - kt);
-        if (later >= 3) vm_wait<3 * C::COPIES_PER_WAVE>();
-        else if (later == 2) vm_wait<2 * C::COPIES_PER_WAVE>();
-        else if (later == 1) vm_wait<C::COPIES_PER_WAVE>();
-        else vm_wait<0>();
-        __builtin_amdgcn_s_barrier();
-        if (kt + S - 1 < nkt) issue(kt + S - 1);
+    // One k-step: this wave's fragments of stage kt (both 16-column halves)
+    // are read first, then (do_issue) the copies of stage kt+S-1 are issued,
+    // then the 16 MFMAs; the compiler overlaps the second half's reads and
+    // the copies with the first half's MFMAs. Every row is computed, pad rows
+    // included (the epilogue drops them): branches around the MFMAs cost more
+    // than skipping pad-only accumulator tiles saves.
+    auto kstep = [&](int kt, auto do_issue) {
         const char* stage = smem + (kt % S) * C::STAGE_BYTES;
-        if (n_live == 0) continue;
+        u32x4 fa[2][C::TM], fb[2][C::TN];
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-            u32x4 fa[C::TM], fb[C::TN];
             const int chunk = 2 * ks + lane / 32;
 #pragma unroll
             for (int i = 0; i < C::TM; ++i) {
@@ -396,20 +380,47 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_wide_kernel(
                 // gathered rows: swizzled row-major; act: fragment blocks
                 const int off = C::GATED ? r * 64 + ((chunk ^ ((r >> 2) & 3)) * 16)
                                          : (r / 16) * 1024 + (chunk * 16 + r % 16) * 16;
-                if (i < n_live) fa[i] = *(const u32x4*)(stage + off);
+                fa[ks][i] = *(const u32x4*)(stage + off);
             }
 #pragma unroll
             for (int t = 0; t < C::TN; ++t) {
                 const int band = (lane % 32) < 16 ? band_lo[t] : band_hi[t];
-                fb[t] = *(const u32x4*)(stage + C::A_BYTES + band * 1024 + (chunk * 16 + lane % 16) * 16);
+                fb[ks][t] = *(const u32x4*)(stage + C::A_BYTES + band * 1024 + (chunk * 16 + lane % 16) * 16);
             }
+        }
+        if constexpr (decltype(do_issue)::value) issue(kt + S - 1);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
             for (int i = 0; i < C::TM; ++i)
-                if (i < n_live) {
 #pragma unroll
-                    for (int t = 0; t < C::TN; ++t) acc[i][t] = mfma32x32x16(fa[i], fb[t], acc[i][t]);
-                }
+                for (int t = 0; t < C::TN; ++t) acc[i][t] = mfma32x32x16(fa[ks][i], fb[ks][t], acc[i][t]);
+    };
+
+    // Prologue: the first S-1 stages (when K has fewer k-steps, the extra
+    // stages repeat the last one into buffers that are never read).
+#pragma unroll
+    for (int p = 0; p < S - 1; ++p) issue(min(p, nkt - 1));
+    if (nkt >= S - 1) {
+        // Steady state: wait for this wave's copies of stage kt (those of the
+        // S-2 later stages stay in flight), publish it with a bare barrier,
+        // and refill the buffer every wave finished with at the previous step.
+        int kt = 0;
+        for (; kt < nkt - (S - 1); ++kt) {
+            vm_wait<(S - 2) * C::COPIES_PER_WAVE>();
+            __builtin_amdgcn_s_barrier();
+            kstep(kt, std::true_type{});
         }
+        // The last S-1 stages: no more copies, so fewer remain in flight.
+        static_for<0, S - 1>([&](auto j) {
+            vm_wait<(S - 2 - decltype(j)::value) * C::COPIES_PER_WAVE>();
+            __builtin_amdgcn_s_barrier();
+            kstep(kt + decltype(j)::value, std::false_type{});
+        });
+    } else {
+        vm_wait<0>();
+        __builtin_amdgcn_s_barrier();
+        for (int kt = 0; kt < nkt; ++kt) kstep(kt, std::false_type{});
     }
 
     // The stages are free once every wave is done with the last one: they
@@ -690,7 +701,7 @@ static int dispatch_gemm(int32_t block_m, const void* a, const void* w, const in
             return launch_wide<WideCfg<GATED, 64, 4>, Y16>(a, w, sorted_ids, block_expert, num_padded, k, n_pairs, K,
                                                       N_out, cap, out, s, what);
         case 128:
-            return launch_wide<WideCfg<GATED, 128, 3>, Y16>(a, w, sorted_ids, block_expert, num_padded, k, n_pairs, K,
+            return launch_wide<WideCfg<GATED, 128, GATED ? 4 : 3>, Y16>(a, w, sorted_ids, block_expert, num_padded, k, n_pairs, K,
                                                        N_out, cap, out, s, what);
     }
     return set_error(MOE_ERR_UNSUPPORTED, "%s: block_m=%d not in {16,32,64,128}", what, block_m);

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace moe {
 
 constexpr int kWave = 64;
@@ -97,6 +99,16 @@ __device__ __forceinline__ void store_y(void* y, int64_t idx, float v) {
         ((_Float16*)y)[idx] = (_Float16)v;
     else
         ((float*)y)[idx] = v;
+}
+
+// f(std::integral_constant<int, I>{}) for I = B .. E-1, unrolled at compile
+// time (for counts that must be template arguments, such as vm_wait's).
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(f);
+    }
 }
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
