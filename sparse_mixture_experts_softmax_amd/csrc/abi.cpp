@@ -36,6 +36,19 @@ int ensure_dynamic_lds(const void* kernel, int bytes, std::atomic<uint64_t>& don
     return MOE_OK;
 }
 
+int device_cu_count(const char* what) {
+    static std::atomic<int> cached[64];
+    int dev = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess) return set_error(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(err));
+    int n = cached[dev & 63].load(std::memory_order_relaxed);
+    if (n > 0) return n;
+    err = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+    if (err != hipSuccess) return set_error(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(err));
+    cached[dev & 63].store(n, std::memory_order_relaxed);
+    return n;
+}
+
 bool valid_block_m(int32_t block_m) { return block_m == 16 || block_m == 32 || block_m == 64 || block_m == 128; }
 
 int check_shape(const char* fn, int64_t T, int32_t H, int32_t E, int32_t k, int32_t I) {

@@ -26,6 +26,10 @@ constexpr int kMaxTopK = 32;
 // (thread-safe: a race only repeats the idempotent attribute call).
 int ensure_dynamic_lds(const void* kernel, int bytes, std::atomic<uint64_t>& done, const char* what);
 
+// Compute units of the current device (cached per device), or a negative
+// MOE_ERR_HIP code with the message set.
+int device_cu_count(const char* what);
+
 // Shared limits on (T, H, E, k, I); I < 0 means "not used by this call".
 int check_shape(const char* fn, int64_t T, int32_t H, int32_t E, int32_t k, int32_t I);
 bool valid_block_m(int32_t block_m);

@@ -288,12 +288,17 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_wide_kernel(
     const int m_real = *num_padded / BM;
     const int64_t real = (int64_t)m_real * n_tiles;
     const int64_t share = (real + 7) / 8;
-    const int64_t logical = (int64_t)(blockIdx.x % 8) * share + blockIdx.x / 8;
-    if ((int64_t)(blockIdx.x / 8) >= share || logical >= real) return;
+    // Persistent: the gridDim.x/8 workgroups of an XCD walk its share of the
+    // tiles in steps of gridDim.x/8, so at any time they hold consecutive
+    // tiles (the row blocks of one expert together), and a workgroup's
+    // stores drain while it starts its next tile.
+    const int xcd = blockIdx.x % 8;
+    const int64_t t_end = min((int64_t)(xcd + 1) * share, real);
+    for (int64_t logical = (int64_t)xcd * share + blockIdx.x / 8; logical < t_end; logical += gridDim.x / 8) {
     const int tn = (int)(logical % n_tiles);
     const int mb = (int)(logical / n_tiles);
     const int e = block_expert[mb];
-    if (e < 0) return;
+    if (e < 0) continue;
     const int64_t w_rows = C::GATED ? 2 * (int64_t)N_out : (int64_t)N_out;
     const int bands = (int)(w_rows / 16);
     const uint16_t* we = w + (int64_t)e * w_rows * K;
@@ -474,8 +479,9 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_wide_kernel(
             const int col = tn * C::COLS + kb * 32;
             const u32x4 v = *(const u32x4*)(stile + (r * CPR + (chunk ^ (r & 15))) * 16);
             if (col < N_out)
-                *(u32x4*)((uint16_t*)out +
-                          ((int64_t)(mb * (BM / 16) + band) * (N_out / 32) + col / 32) * 512 + l * 8) = v;
+                __builtin_nontemporal_store(
+                    v, (u32x4*)((uint16_t*)out + ((int64_t)(mb * (BM / 16) + band) * (N_out / 32) + col / 32) * 512 +
+                                l * 8));
         }
     } else {
         // 32-row passes (one accumulator tile row of the waves of one wm)
@@ -504,10 +510,13 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_wide_kernel(
                 const int r = ci / CPR, col = tn * C::COLS + (ci % CPR) * (16 / ES);
                 const int32_t id = ids_s[pass * 32 + r];
                 const u32x4 v = *(const u32x4*)(stile + ci * 16);
-                if (real_row(id) && col < N_out) *(u32x4*)((char*)out + ((int64_t)id * N_out + col) * ES) = v;
+                if (real_row(id) && col < N_out)
+                    __builtin_nontemporal_store(v, (u32x4*)((char*)out + ((int64_t)id * N_out + col) * ES));
             }
             __syncthreads();
         }
+    }
+    __syncthreads();  // the next tile's copies reuse the staging memory
     }
 }
 
@@ -516,8 +525,13 @@ static int launch_wide(const void* a, const void* w, const int32_t* sorted_ids, 
                        const int32_t* num_padded, int k, int64_t n_pairs, int K, int N_out, int64_t cap, void* out,
                        hipStream_t s, const char* what) {
     const int n_tiles = (N_out + C::COLS - 1) / C::COLS;
+    // one workgroup per compute unit at most (160 KB of LDS each), a multiple
+    // of 8 so that every XCD gets the same number
+    const int cus = device_cu_count(what);
+    if (cus < 0) return cus;
     int64_t grid = (cap / C::BM) * n_tiles;
     grid = (grid + 7) / 8 * 8;
+    grid = min(grid, (int64_t)max(8, cus / 8 * 8));
     if (grid >= ((int64_t)1 << 31)) return set_error(MOE_ERR_UNSUPPORTED, "%s: grid too large", what);
     const size_t lds = (size_t)C::STAGES * C::STAGE_BYTES;
     static std::atomic<uint64_t> lds_set{0};
