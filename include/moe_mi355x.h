@@ -43,7 +43,9 @@
  *    returns a thread-local message describing the last failure.
  *  - Limits: 1 <= E <= 256, 1 <= k <= min(E, 32), H % 64 == 0, I % 32 == 0,
  *    T >= 0 (T == 0 is a successful no-op), T * k < 2^31,
- *    block_m in {16, 32, 64, 128}.
+ *    block_m in {16, 32, 64, 128}; with block_m 64 or 128 the grouped GEMMs'
+ *    activation operand (x: T*H*2 bytes; act: cap*I*2 bytes) and one expert's
+ *    weights must each be under 4 GiB (the copies use 32-bit offsets).
  */
 #ifndef MOE_MI355X_H
 #define MOE_MI355X_H

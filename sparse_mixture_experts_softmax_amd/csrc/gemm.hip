@@ -283,7 +283,8 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_wide_kernel(
     constexpr int BM = C::BM, S = C::STAGES;
     extern __shared__ __attribute__((aligned(16))) char smem[];
 
-    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    const int tid = threadIdx.x, lane = tid % kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // uniform: copy bases and LDS slots in SGPRs
     // XCD-aware tile order over the real tiles only
     const int m_real = *num_padded / BM;
     const int64_t real = (int64_t)m_real * n_tiles;
@@ -307,8 +308,15 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_wide_kernel(
     auto real_row = [&](int32_t id) { return id >= 0 && (int64_t)id < n_pairs; };
     const int32_t my_id = tid < BM ? ids_blk[tid] : 0;  // row ids for the epilogue (C::THREADS >= BM)
 
-    // This wave's copies: index q over [A rows 16q.. | B band q - BM/16].
-    const uint16_t* src[C::COPIES_PER_WAVE];
+    // This wave's copies: index q over [A rows 16q.. | B band q - BM/16],
+    // each a uniform base (the activations or this expert's weights) plus a
+    // 32-bit per-lane byte offset (operands are under 4 GiB, checked on the
+    // host), so the copies use the SGPR-base form and take half the address
+    // registers of 64-bit pointers.
+    typedef uint32_t copy_off_t;
+    const char* const base_a = (const char*)a_src;
+    const char* const base_b = (const char*)we;
+    copy_off_t soff[C::COPIES_PER_WAVE];
     int dst[C::COPIES_PER_WAVE];  // byte offset inside a stage (wave-uniform)
 #pragma unroll
     for (int j = 0; j < C::COPIES_PER_WAVE; ++j) {
@@ -320,16 +328,16 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_wide_kernel(
                 const int chunk = (lane % 4) ^ ((row >> 2) & 3);  // LDS slot lane%4 holds this chunk
                 const int32_t id = ids_blk[row];
                 const int64_t base = real_row(id) ? (int64_t)(id / k) * K : 0;  // sentinel rows: any valid row
-                src[j] = a_src + base + chunk * 8;
+                soff[j] = (copy_off_t)((base + chunk * 8) * 2);
             } else {
                 // one 1 KB act fragment block (16 rows x 32 columns)
-                src[j] = a_src + (int64_t)(mb * (BM / 16) + q) * (K / 32) * 512 + lane * 8;
+                soff[j] = (copy_off_t)(((int64_t)(mb * (BM / 16) + q) * (K / 32) * 512 + lane * 8) * 2);
             }
             dst[j] = q * 1024;
         } else {
             const int bt = q - BM / 16;
             const int band = min(tn * (C::BN / 16) + bt, bands - 1);
-            src[j] = we + (int64_t)band * 16 * K + lane * 8;
+            soff[j] = (copy_off_t)(((int64_t)band * 16 * K + lane * 8) * 2);
             dst[j] = C::A_BYTES + bt * 1024;
         }
     }
@@ -339,9 +347,10 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_wide_kernel(
 #pragma unroll
         for (int j = 0; j < C::COPIES_PER_WAVE; ++j) {
             const int q = wave * C::COPIES_PER_WAVE + j;
-            // gathered rows: 32 columns on; fragment blocks: the next block
-            const int64_t step = (q < BM / 16 && C::GATED) ? 32 : 512;
-            lds_dma16(src[j] + kt * step, stage + dst[j]);
+            const bool is_a = q < BM / 16;
+            // gathered rows: 32 columns (64 bytes) on; fragment blocks: the next 1 KB block
+            const copy_off_t step = (is_a && C::GATED) ? 64 : 1024;
+            lds_dma16((is_a ? base_a : base_b) + (soff[j] + (copy_off_t)kt * step), stage + dst[j]);
         }
     };
 
@@ -525,6 +534,16 @@ static int launch_wide(const void* a, const void* w, const int32_t* sorted_ids, 
                        const int32_t* num_padded, int k, int64_t n_pairs, int K, int N_out, int64_t cap, void* out,
                        hipStream_t s, const char* what) {
     const int n_tiles = (N_out + C::COLS - 1) / C::COLS;
+    // The copies take 32-bit offsets: the activation rows they address
+    // (gathered x rows, T = n_pairs / k of them, for gate/up; the act rows of
+    // the capacity for down) and one expert's weights must be under 4 GiB.
+    const int64_t a_bytes = (C::GATED ? n_pairs / k : cap) * (int64_t)K * 2;
+    const int64_t w_bytes = (C::GATED ? 2 : 1) * (int64_t)N_out * K * 2;  // one expert's weights
+    if (a_bytes >= ((int64_t)1 << 32) || w_bytes >= ((int64_t)1 << 32))
+        return set_error(MOE_ERR_UNSUPPORTED,
+                         "%s: block_m=%d needs the activations (%lld bytes) and one expert's weights (%lld bytes) "
+                         "under 4 GiB; split the batch",
+                         what, C::BM, (long long)a_bytes, (long long)w_bytes);
     // one workgroup per compute unit at most (160 KB of LDS each), a multiple
     // of 8 so that every XCD gets the same number
     const int cus = device_cu_count(what);

@@ -103,6 +103,16 @@ def test_gemm_validation():
         misaligned = ctypes.c_void_p(0x1002)
         assert fn(misaligned, FAKE, FAKE, FAKE, FAKE, 16, 2, 64, 32, 8, 16, cap, FAKE, NULL) == _lib.MOE_ERR_INVALID
         assert fn(NULL, NULL, NULL, NULL, NULL, 0, 2, 64, 32, 8, 16, 0, NULL, NULL) == _lib.MOE_OK
+    # block_m 64/128: activations over 4 GiB are refused before any launch
+    # (x of T=2^21 tokens at H=2048 is 8 GiB)
+    big_T = 1 << 21
+    cap = moe.moe_align_capacity(big_T, 2, 8, 128)
+    assert L.moe_grouped_gemm_gate_up_silu(FAKE, FAKE, FAKE, FAKE, FAKE, big_T, 2, 2048, 32, 8, 128, cap, FAKE,
+                                           NULL) == _lib.MOE_ERR_UNSUPPORTED
+    assert "4 GiB" in moe.moe_last_error()
+    assert L.moe_grouped_gemm_down(FAKE, FAKE, FAKE, FAKE, FAKE, big_T, 2, 64, 2048, 8, 128, cap, FAKE, F16,
+                                   NULL) == _lib.MOE_ERR_UNSUPPORTED
+    assert "4 GiB" in moe.moe_last_error()
     # y is fp16 or fp32, nothing else (bf16 included)
     cap = moe.moe_align_capacity(16, 2, 8, 16)
     for bad in (_lib.MOE_DTYPE_BF16, 3, -1):
