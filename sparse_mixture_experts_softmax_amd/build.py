@@ -11,6 +11,7 @@ from __future__ import annotations
 import argparse
 import concurrent.futures
 import os
+import re
 import subprocess
 import sys
 
@@ -40,12 +41,35 @@ def hipcc() -> str:
     return path if os.path.exists(path) else "hipcc"
 
 
+def _scratch_users(remarks: str) -> list:
+    """Kernels whose resource-usage remark reports scratch (register spills).
+
+    The copy pipelines count their outstanding memory operations by hand
+    (s_waitcnt vmcnt), so a spill reload inside a loop would break the count;
+    every kernel here must run without scratch.
+    """
+    bad, name = [], None
+    for line in remarks.splitlines():
+        m = re.search(r"remark: Function Name: (\S+)", line)
+        if m:
+            name = m.group(1)
+            continue
+        m = re.search(r"remark:\s+ScratchSize \[bytes/lane\]: (\d+)", line)
+        if m and int(m.group(1)) > 0:
+            bad.append(f"{name} ({m.group(1)} bytes/lane)")
+    return bad
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *HIP_FLAGS, f"-I{INCLUDE}", f"-I{CSRC}", "-c", os.path.join(CSRC, src), "-o", obj]
+    remarks = ["-Rpass-analysis=kernel-resource-usage"] if src.endswith(".hip") else []
+    cmd = [hipcc(), *HIP_FLAGS, *remarks, f"-I{INCLUDE}", f"-I{CSRC}", "-c", os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{res.stdout}\n{res.stderr}")
+    bad = _scratch_users(res.stderr)
+    if bad:
+        raise RuntimeError(f"{src}: kernels use scratch (register spills): " + ", ".join(bad))
     return obj
 
 

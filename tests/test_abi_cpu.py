@@ -178,3 +178,14 @@ def test_header_abi_version_matches_library():
     with open(os.path.join(root, "include", "moe_mi355x.h")) as fh:
         header_version = int(re.search(r"#define MOE_ABI_VERSION (\d+)", fh.read()).group(1))
     assert moe.moe_abi_version() == header_version
+
+
+def test_build_rejects_scratch():
+    # the build fails when a kernel's resource-usage remark reports scratch
+    from sparse_mixture_experts_softmax_amd import build
+    clean = ("a.hip:1:1: remark: Function Name: _Z1kv [-Rpass-analysis=kernel-resource-usage]\n"
+             "a.hip:1:1: remark:     ScratchSize [bytes/lane]: 0 [-Rpass-analysis=kernel-resource-usage]\n")
+    spill = clean + ("a.hip:9:1: remark: Function Name: _Z1jv [-Rpass-analysis=kernel-resource-usage]\n"
+                     "a.hip:9:1: remark:     ScratchSize [bytes/lane]: 36 [-Rpass-analysis=kernel-resource-usage]\n")
+    assert build._scratch_users(clean) == []
+    assert build._scratch_users(spill) == ["_Z1jv (36 bytes/lane)"]
