@@ -4,7 +4,8 @@
 // Two kernels. router_logits_kernel: one workgroup per (16 tokens, 16*NTW
 // experts) tile, the H dimension split in four contiguous slices over the
 // workgroup's four waves; each wave issues its slice's 16-byte loads in
-// batches of eight k-steps and accumulates with v_mfma_f32_16x16x32_bf16;
+// batches of k-steps (16 for small batches, 8 for large) and accumulates
+// with v_mfma_f32_16x16x32_bf16;
 // the four partials are summed in LDS in a fixed order, so the logits do not
 // depend on scheduling. Small batches use one expert tile per workgroup (many
 // workgroups pull the router weight in parallel); large ones use eight, so
@@ -22,13 +23,14 @@ constexpr int kRouteTokens = 16;  // tokens per logits tile (the MFMA M size)
 constexpr int kRouteSlices = 4;   // waves per logits workgroup = slices of H
 constexpr int kTopkWaves = 4;     // tokens per top-k workgroup
 
-template <int NTW>
+template <int NTW, int U>
 __global__ __launch_bounds__(kRouteSlices* kWave) void router_logits_kernel(const uint16_t* __restrict__ x,
                                                                             const uint16_t* __restrict__ wr,
                                                                             const float* __restrict__ bias,
                                                                             float* __restrict__ logits, int64_t T,
                                                                             int H, int E) {
-    constexpr int U = 8;  // k-steps per batch of loads
+    // U: k-steps per batch of loads (all loads of a batch are issued before
+    // the first MFMA: one memory wait per batch)
     constexpr int COLS = 16 * NTW;
     __shared__ float part[kRouteSlices][kRouteTokens][COLS + 1];
     const int lane = threadIdx.x % kWave, slice = threadIdx.x / kWave;
@@ -371,11 +373,12 @@ extern "C" int moe_route(const void* x, const void* w_router, const float* route
                                : launch_route_wide<3>(grid, x, w_router, router_bias, logits, T, H, E, s);
             if (rc) return rc;
         } else if (T <= 256 || ntiles < 8) {
-            hipLaunchKernelGGL(router_logits_kernel<1>, dim3((unsigned)tblocks, (unsigned)ntiles),
+            // one batch of loads per slice at H = 2048 (16 k-steps)
+            hipLaunchKernelGGL((router_logits_kernel<1, 16>), dim3((unsigned)tblocks, (unsigned)ntiles),
                                dim3(kRouteSlices * kWave), 0, s, (const uint16_t*)x, (const uint16_t*)w_router,
                                router_bias, logits, T, (int)H, (int)E);
         } else {
-            hipLaunchKernelGGL(router_logits_kernel<8>, dim3((unsigned)tblocks, (unsigned)((ntiles + 7) / 8)),
+            hipLaunchKernelGGL((router_logits_kernel<8, 8>), dim3((unsigned)tblocks, (unsigned)((ntiles + 7) / 8)),
                                dim3(kRouteSlices * kWave), 0, s, (const uint16_t*)x, (const uint16_t*)w_router,
                                router_bias, logits, T, (int)H, (int)E);
         }
