@@ -323,14 +323,15 @@ __global__ __launch_bounds__(kTopkWaves* kWave) void route_topk_kernel(const flo
     }
 }
 
-template <int NB>
-static int launch_route_wide(dim3 grid, const void* x, const void* w_router, const float* bias, float* logits,
-                             int64_t T, int32_t H, int32_t E, hipStream_t s) {
-    constexpr int lds = RouteWide<2, NB>::NB * RouteWide<2, NB>::CHUNK_BYTES;
+template <int ET, int NB>
+static int launch_route_wide(const void* x, const void* w_router, const float* bias, float* logits, int64_t T,
+                             int32_t H, int32_t E, int ntiles, hipStream_t s) {
+    const dim3 grid((unsigned)((T + kRouteWideTokens - 1) / kRouteWideTokens), (unsigned)((ntiles + ET - 1) / ET));
+    constexpr int lds = RouteWide<ET, NB>::NB * RouteWide<ET, NB>::CHUNK_BYTES;
     static std::atomic<uint64_t> lds_set{0};
-    const int rc = ensure_dynamic_lds((const void*)router_logits_wide_kernel<2, NB>, lds, lds_set, "moe_route");
+    const int rc = ensure_dynamic_lds((const void*)router_logits_wide_kernel<ET, NB>, lds, lds_set, "moe_route");
     if (rc) return rc;
-    hipLaunchKernelGGL((router_logits_wide_kernel<2, NB>), grid, dim3(kRouteSlices * kWave), lds, s,
+    hipLaunchKernelGGL((router_logits_wide_kernel<ET, NB>), grid, dim3(kRouteSlices * kWave), lds, s,
                        (const uint16_t*)x, (const uint16_t*)w_router, bias, logits, T, (int)H, (int)E);
     return MOE_OK;
 }
@@ -365,12 +366,20 @@ extern "C" int moe_route(const void* x, const void* w_router, const float* route
         if (tblocks >= ((int64_t)1 << 31)) return set_error(MOE_ERR_UNSUPPORTED, "moe_route: T too large");
         const int ksteps = H / 32;
         if (T > 256 && ksteps % (kRouteSlices * kRouteChunk) == 0) {
-            // one round of workgroups on the 256 CUs: the deepest ring (one
-            // workgroup per CU); more: a shallower ring, two per CU
-            const dim3 grid((unsigned)((T + kRouteWideTokens - 1) / kRouteWideTokens), (unsigned)((ntiles + 1) / 2));
-            const int rc = (int64_t)grid.x * grid.y <= 256
-                               ? launch_route_wide<6>(grid, x, w_router, router_bias, logits, T, H, E, s)
-                               : launch_route_wide<3>(grid, x, w_router, router_bias, logits, T, H, E, s);
+            // Each workgroup re-reads its 64 activation rows once per group
+            // of 16*ET experts, so ET is as large as still gives a full round
+            // of workgroups on the 256 CUs (one per CU, the deepest ring);
+            // below that, ET = 2 with a shallower ring, two per CU.
+            const int64_t tg = (T + kRouteWideTokens - 1) / kRouteWideTokens;
+            int rc;
+            if (tg * ((ntiles + 7) / 8) >= 256)
+                rc = launch_route_wide<8, 3>(x, w_router, router_bias, logits, T, H, E, ntiles, s);
+            else if (tg * ((ntiles + 3) / 4) >= 256)
+                rc = launch_route_wide<4, 4>(x, w_router, router_bias, logits, T, H, E, ntiles, s);
+            else if (tg * ((ntiles + 1) / 2) <= 256)
+                rc = launch_route_wide<2, 6>(x, w_router, router_bias, logits, T, H, E, ntiles, s);
+            else
+                rc = launch_route_wide<2, 3>(x, w_router, router_bias, logits, T, H, E, ntiles, s);
             if (rc) return rc;
         } else if (T <= 256 || ntiles < 8) {
             // one batch of loads per slice at H = 2048 (16 k-steps)

@@ -79,10 +79,12 @@ def test_route_ties_from_given_logits(E, k, norm):
     assert np.array_equal(logits.cpu().numpy(), lg)  # logits are input only
 
 
-@pytest.mark.parametrize("T,H,E", [(333, 512, 40), (1000, 2048, 128), (300, 4096, 256), (17000, 512, 32)])
+@pytest.mark.parametrize("T,H,E", [(333, 512, 40), (1000, 2048, 128), (300, 4096, 256), (17000, 512, 32),
+                                   (8192, 512, 128), (16384, 512, 128)])
 def test_router_logits_same_bits_for_small_and_large_batches(T, H, E):
-    """Batches above 256 tokens take the workgroup-shared router kernel; a
-    token's logits must not depend on which kernel (batch size) computed
+    """Batches above 256 tokens take the workgroup-shared router kernel (32,
+    64 or 128 experts per workgroup as the batch grows: the last two cases);
+    a token's logits must not depend on which kernel (batch size) computed
     them, and both must match the oracle."""
     inp = custom_inputs(f"router{T}", T, H, E, min(8, E), 64, seed=T + H)
     dev = device_inputs(inp)
