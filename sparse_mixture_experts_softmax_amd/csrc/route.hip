@@ -9,11 +9,12 @@
 // the four partials are summed in LDS in a fixed order, so the logits do not
 // depend on scheduling. Small batches use one expert tile per workgroup (many
 // workgroups pull the router weight in parallel); large ones use eight, so
-// the activation rows are re-read less often. route_topk_kernel: one wave
-// per token; each lane holds up to four of the token's logits, and each of
-// the k arg-max rounds and the softmax sums are wave reductions on DPP lane
-// permutations (no LDS). Selection uses the fp32 logits, so it is exact given
-// them.
+// the activation rows are re-read less often. Top-k: for k <= 16,
+// route_topk_row_kernel gives each token one 16-lane row of a wave; above,
+// route_topk_kernel gives it a whole wave (each lane holding up to four of
+// the token's logits). Each of the k arg-max rounds and the softmax sums are
+// reductions on DPP lane permutations (no LDS). Selection uses the fp32
+// logits, so it is exact given them.
 #include "abi_util.h"
 #include "moe_common.h"
 
@@ -323,6 +324,78 @@ __global__ __launch_bounds__(kTopkWaves* kWave) void route_topk_kernel(const flo
     }
 }
 
+// The same selection with 16 lanes (one DPP row) per token, four tokens per
+// wave, for k <= 16: every reduction stays inside a row, so no v_readlane,
+// and a quarter of the waves. Lane r of a row holds experts r, r+16, ...
+// (PER of them) and keeps pick r. With norm the weights are the same bits
+// as route_topk_kernel's (the same four DPP steps over the same values).
+constexpr int kTopkRowTokens = 16;  // tokens per workgroup (4 waves x 4 rows)
+
+__device__ __forceinline__ uint64_t row_max_u64(uint64_t v) {
+    v = max_dpp<kDppXor1>(v);
+    v = max_dpp<kDppXor2>(v);
+    v = max_dpp<kDppHalfMirror>(v);
+    return max_dpp<kDppMirror>(v);
+}
+
+__device__ __forceinline__ float row_sum(float v) {
+    v = add_dpp<kDppXor1>(v);
+    v = add_dpp<kDppXor2>(v);
+    v = add_dpp<kDppHalfMirror>(v);
+    return add_dpp<kDppMirror>(v);
+}
+
+template <int PER>
+__global__ __launch_bounds__(kTopkWaves* kWave) void route_topk_row_kernel(const float* __restrict__ logits,
+                                                                           int32_t* __restrict__ topk_ids,
+                                                                           float* __restrict__ topk_w, int64_t T,
+                                                                           int E, int k, int norm) {
+    const int r = threadIdx.x % 16;
+    const int64_t t = (int64_t)blockIdx.x * kTopkRowTokens + threadIdx.x / 16;
+    if (t >= T) return;  // the whole row leaves together
+    const float* row = logits + t * E;
+    float v[PER];
+    uint64_t key[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int e = r + 16 * i;
+        v[i] = row[min(e, E - 1)];
+        key[i] = e < E ? select_key(v[i], e) : 0;
+    }
+    int my_id = 0;
+    float my_val = 0.f, mx = 0.f;
+    for (int j = 0; j < k; ++j) {
+        uint64_t best = key[0];
+#pragma unroll
+        for (int i = 1; i < PER; ++i) best = key[i] > best ? key[i] : best;
+        best = row_max_u64(best);
+        const int e = (int)~(uint32_t)best;
+#pragma unroll
+        for (int i = 0; i < PER; ++i)
+            if (r + 16 * i == e) key[i] = 0;
+        const float lv = key_logit(best);
+        if (j == 0) mx = lv;  // softmax: the largest logit is the first pick
+        if (r == j) {
+            my_id = e;
+            my_val = lv;
+        }
+    }
+    const float ex = r < k ? expf(my_val - mx) : 0.f;
+    float denom;
+    if (norm) {
+        denom = row_sum(ex);
+    } else {
+        float z = 0.f;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) z += r + 16 * i < E ? expf(v[i] - mx) : 0.f;
+        denom = row_sum(z);
+    }
+    if (r < k) {
+        topk_ids[t * k + r] = my_id;
+        topk_w[t * k + r] = ex / denom;
+    }
+}
+
 template <int ET, int NB>
 static int launch_route_wide(const void* x, const void* w_router, const float* bias, float* logits, int64_t T,
                              int32_t H, int32_t E, int ntiles, hipStream_t s) {
@@ -396,6 +469,16 @@ extern "C" int moe_route(const void* x, const void* w_router, const float* route
     }
     const int64_t blocks = (T + kTopkWaves - 1) / kTopkWaves;
     if (blocks >= ((int64_t)1 << 31)) return set_error(MOE_ERR_UNSUPPORTED, "moe_route: T too large");
+    if (k <= 16) {
+        const dim3 grid((unsigned)((T + kTopkRowTokens - 1) / kTopkRowTokens)), block(kTopkWaves * kWave);
+        if (E <= 128)
+            hipLaunchKernelGGL((route_topk_row_kernel<8>), grid, block, 0, s, logits, topk_ids, topk_weights, T, (int)E,
+                               (int)k, (int)(norm_topk_prob != 0));
+        else
+            hipLaunchKernelGGL((route_topk_row_kernel<16>), grid, block, 0, s, logits, topk_ids, topk_weights, T,
+                               (int)E, (int)k, (int)(norm_topk_prob != 0));
+        return check_launch("moe_route (top-k)");
+    }
     hipLaunchKernelGGL(route_topk_kernel, dim3((unsigned)blocks), dim3(kTopkWaves * kWave), 0, s, logits, topk_ids,
                        topk_weights, T, (int)E, (int)k, (int)(norm_topk_prob != 0));
     return check_launch("moe_route (top-k)");

@@ -62,9 +62,11 @@ def test_route_bitexact_given_logits(name):
 
 
 @pytest.mark.parametrize("E,k,norm", [(8, 2, True), (128, 8, True), (128, 8, False), (256, 32, True), (5, 5, False),
-                                      (1, 1, True)])
+                                      (1, 1, True), (256, 16, True), (200, 8, False), (129, 17, True)])
 def test_route_ties_from_given_logits(E, k, norm):
-    """Integer-valued logits force ties: lower expert index first."""
+    """Integer-valued logits force ties: lower expert index first. k <= 16
+    takes the 16-lanes-per-token kernel (8 or 16 logits per lane), larger k
+    the wave-per-token one."""
     rng = np.random.default_rng(E * 100 + k)
     T = 203
     lg = rng.integers(-3, 4, size=(T, E)).astype(np.float32)
