@@ -15,9 +15,10 @@
 //   16       grouped_gemm_skinny_kernel (weight streaming, decode-sized)
 //   32       grouped_gemm_kernel        (16x16x32 MFMA, LDS-staged)
 //   64, 128  grouped_gemm_wide_kernel   (32x32x16 MFMA, direct-to-LDS copies)
-// Grids cover one workgroup per (row block, N tile) of the capacity; blocks
-// past num_padded (read on the device) return at once, so no host sync is
-// needed.
+// The skinny and general kernels launch one workgroup per (row block, N
+// tile) of the capacity and blocks past num_padded (read on the device)
+// return at once; the wide kernel launches one persistent workgroup per CU
+// that walks the real tiles. Either way no host sync is needed.
 //
 // General kernel (row blocks of 32): each workgroup stages BMxBK
 // activation rows (gathered through sorted_ids for gate/up) in padded
@@ -240,9 +241,11 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(
 // the activation rows' columns [32kt, 32kt+32) and one packed 1 KB block per
 // weight band. The A rows are stored 64 bytes apart with their four 16-byte
 // chunks XOR-swizzled by (row/4)%4 so that fragment reads are free of bank
-// conflicts; B blocks are stored as packed. Each wave waits only for its own copies of the stage it
-// needs (explicit vmcnt), then a bare s_barrier publishes the stage to all
-// waves and frees the oldest one for the next copy.
+// conflicts; B blocks are stored as packed. Each copy instruction costs the
+// issuing wave time, so its address is a uniform SGPR base plus a 32-bit
+// lane offset. Each wave waits only for its own copies of the stage it needs
+// (explicit vmcnt), then a bare s_barrier publishes the stage to all waves
+// and frees the oldest one for the next copy.
 //
 // Tiles are ordered so each XCD (workgroups go to the 8 XCDs round robin)
 // takes a contiguous share of the real (row block, N tile) pairs, row-block
