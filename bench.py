@@ -26,6 +26,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -61,11 +62,19 @@ def progress(msg: str):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+def _code_only(text: str) -> str:
+    """Source text without comments and with whitespace collapsed, so that a
+    comment edit does not count as a change of the kernel."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def source_hash(kernel: str) -> str:
     h = hashlib.sha256()
     for f in KERNEL_SOURCES[kernel]:
-        with open(os.path.join(ROOT, "sparse_mixture_experts_softmax_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "sparse_mixture_experts_softmax_amd", "csrc", f), encoding="utf-8") as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -230,10 +230,11 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(
 
 // Wide variant for row blocks of 64 or 128 (tens to thousands of rows per
 // expert, as in prefill): matrix-core bound, so it runs on
-// v_mfma_f32_32x32x16_bf16 (on gfx950 the 16x16x32 form issues at about half
-// the rate) with 64x128 wave tiles (2x4 accumulator tiles of 32x32, 128
+// v_mfma_f32_32x32x16_bf16 (half the MFMA instructions of the 16x16x32 form
+// for the same work, which leaves issue slots to the copies and fragment
+// reads) with 64x128 wave tiles (2x4 accumulator tiles of 32x32, 128
 // accumulator registers); the workgroup covers BM rows x 512 weight rows
-// with (BM/64) x 4 waves.
+// with (BM/64) x 4 waves, two waves per SIMD.
 //
 // Operands reach LDS by direct global->LDS copies (global_load_lds_dwordx4,
 // no registers), S stages deep (128-row blocks: 4 for gate/up, all 160 KB of
