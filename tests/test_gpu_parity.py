@@ -297,6 +297,10 @@ def test_layer_edge_cases():
         ("wide", 33, 1024, 256, 32, 32, True),
         ("no_renorm", 50, 192, 12, 3, 160, False),
         ("multi_tile", 600, 64, 16, 8, 64, True),
+        # 128-row blocks through the pipelined wide kernel with ragged N
+        # tiles (I and H below one tile) and an odd k-step count (I/32 = 5)
+        ("wide_ragged", 700, 192, 8, 2, 160, True),
+        ("wide_odd", 520, 128, 4, 1, 96, False),
     ]
     for name, T, H, E, k, I, norm in cases:
         log(f"edge {name}")
