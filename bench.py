@@ -367,8 +367,8 @@ def main():
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4)}
     roof["kernel"] = ("moe_grouped_gemm_gate_up_silu: " +
                       {16: "grouped_gemm_skinny_kernel<true,1,2,8>", 32: "grouped_gemm_kernel<GemmCfg<32,128,true>>",
-                       64: "grouped_gemm_wide_kernel<WideCfg<true,64,4>>",
-                       128: "grouped_gemm_wide_kernel<WideCfg<true,128,4>>"}[block_m])
+                       64: "grouped_gemm_wide_kernel<WideCfg<true,64,4,4,2,128>,false,false>",
+                       128: "grouped_gemm_wide_kernel<WideCfg<true,128,4,4,2,128>,false,false>"}[block_m])
     roof["kernel_ms"] = round(dom_ms, 5)
     roof["timing"] = (f"HIP events around each of the {args.steps} launches in a second timed region of "
                       f"{args.steps} steps ({elapsed_marked * 1e3 / args.steps:.4f} ms/step with the markers)")

@@ -253,17 +253,18 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(
 // major: the row blocks of one expert run together on one XCD and share its
 // L2 for the weight tile. The epilogue stages the output tile in LDS and
 // stores whole rows.
-template <bool GATED_, int BM_, int STAGES_>
+template <bool GATED_, int BM_, int STAGES_, int WAVES_N_ = 4, int TM_ = 2, int WTN_ = 128>
 struct WideCfg {
     static constexpr bool GATED = GATED_;
     static constexpr int BM = BM_;
-    static constexpr int WAVES_M = BM / 64;
-    static constexpr int WAVES_N = 4;
+    static constexpr int TM = TM_;               // 32-row accumulator tiles per wave
+    static constexpr int WAVES_N = WAVES_N_;
+    static constexpr int WAVES_M = BM / (32 * TM);
     static constexpr int THREADS = WAVES_M * WAVES_N * kWave;
-    static constexpr int WTN = 128;              // weight rows per wave
+    static constexpr int WTN = WTN_;             // weight rows per wave
+    static constexpr int TN = WTN / 32;          // 32-column accumulator tiles per wave
     static constexpr int BN = WAVES_N * WTN;     // weight rows per workgroup
     static constexpr int COLS = GATED ? BN / 2 : BN;  // output columns per workgroup
-    static constexpr int TM = 2, TN = 4;         // 32x32 accumulator tiles per wave
     static constexpr int STAGES = STAGES_;
     static constexpr int A_BYTES = BM * 64;      // one stage of A: BM rows x 32 columns
     static constexpr int B_BYTES = BN * 64;      // BN/16 packed blocks of 1 KB
@@ -271,7 +272,8 @@ struct WideCfg {
     static constexpr int COPIES = (BM + BN) / 16;  // 1 KB copies per stage
     static constexpr int COPIES_PER_WAVE = COPIES / (WAVES_M * WAVES_N);
     static_assert(COPIES % (WAVES_M * WAVES_N) == 0, "copies must split evenly over the waves");
-    static_assert(STAGES >= 2 && STAGES <= 5, "stages");
+    static_assert(STAGES >= 2 && STAGES <= 6, "stages");
+    static_assert((STAGES - 1) * COPIES_PER_WAVE < 64, "vmcnt range");
     static_assert(STAGES * STAGE_BYTES <= 160 * 1024, "LDS");
     static_assert(THREADS >= BM, "one row id per thread");
     // the epilogue reuses the stages: 1 KB of row ids, then the bf16 act tile
@@ -279,31 +281,24 @@ struct WideCfg {
     static_assert(1024 + (GATED ? BM * COLS * 2 : 32 * COLS * 4) <= STAGES * STAGE_BYTES, "epilogue staging");
 };
 
-template <class C, bool Y16>
-__global__ __launch_bounds__(C::THREADS) void grouped_gemm_wide_kernel(
-    const uint16_t* __restrict__ a_src, const uint16_t* __restrict__ w, const int32_t* __restrict__ sorted_ids,
-    const int32_t* __restrict__ block_expert, const int32_t* __restrict__ num_padded, int k, int64_t n_pairs,
-    int K, int N_out, int n_tiles, void* __restrict__ out) {
-    constexpr int BM = C::BM, S = C::STAGES;
-    extern __shared__ __attribute__((aligned(16))) char smem[];
+// Quarter-width tiles of the down projection's 128-row blocks (128 output
+// columns, eight waves as 4 x 2 with 32x64 wave tiles): the last, partial
+// round of tiles of an XCD is handed out as four of these per tile, so it
+// takes about a third of a full tile's time instead of a whole one. Same
+// MFMA and the same k order per element, so the same bits.
+template <int BM_>
+using WideQuarterCfg = WideCfg<false, BM_, 6, 2, 1, 64>;
 
-    const int tid = threadIdx.x, lane = tid % kWave;
-    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // uniform: copy bases and LDS slots in SGPRs
-    // XCD-aware tile order over the real tiles only
-    const int m_real = *num_padded / BM;
-    const int64_t real = (int64_t)m_real * n_tiles;
-    const int64_t share = (real + 7) / 8;
-    // Persistent: the gridDim.x/8 workgroups of an XCD walk its share of the
-    // tiles in steps of gridDim.x/8, so at any time they hold consecutive
-    // tiles (the row blocks of one expert together), and a workgroup's
-    // stores drain while it starts its next tile.
-    const int xcd = blockIdx.x % 8;
-    const int64_t t_end = min((int64_t)(xcd + 1) * share, real);
-    for (int64_t logical = (int64_t)xcd * share + blockIdx.x / 8; logical < t_end; logical += gridDim.x / 8) {
-    const int tn = (int)(logical % n_tiles);
-    const int mb = (int)(logical / n_tiles);
-    const int e = block_expert[mb];
-    if (e < 0) continue;
+// One tile of the wide GEMM: the workgroup's C::BM rows of row block mb
+// (expert e) against C::BN weight rows from band band0 on, written to the
+// output columns from col0 on. smem holds the stages (and, after the k loop,
+// the epilogue's staging); the caller synchronises before reusing it.
+template <class C, bool Y16>
+__device__ __forceinline__ void wide_tile(const uint16_t* __restrict__ a_src, const uint16_t* __restrict__ w,
+                                          const int32_t* __restrict__ sorted_ids, int e, int mb, int band0,
+                                          int col0, int k, int64_t n_pairs, int K, int N_out,
+                                          void* __restrict__ out, char* smem, int tid, int lane, int wave) {
+    constexpr int BM = C::BM, S = C::STAGES;
     const int64_t w_rows = C::GATED ? 2 * (int64_t)N_out : (int64_t)N_out;
     const int bands = (int)(w_rows / 16);
     const uint16_t* we = w + (int64_t)e * w_rows * K;
@@ -340,7 +335,7 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_wide_kernel(
             dst[j] = q * 1024;
         } else {
             const int bt = q - BM / 16;
-            const int band = min(tn * (C::BN / 16) + bt, bands - 1);
+            const int band = min(band0 + bt, bands - 1);
             soff[j] = (copy_off_t)(((int64_t)band * 16 * K + lane * 8) * 2);
             dst[j] = C::A_BYTES + bt * 1024;
         }
@@ -394,7 +389,7 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_wide_kernel(
             const int chunk = 2 * ks + lane / 32;
 #pragma unroll
             for (int i = 0; i < C::TM; ++i) {
-                const int r = wm * 64 + i * 32 + lane % 32;
+                const int r = wm * (32 * C::TM) + i * 32 + lane % 32;
                 // gathered rows: swizzled row-major; act: fragment blocks
                 const int off = C::GATED ? r * 64 + ((chunk ^ ((r >> 2) & 3)) * 16)
                                          : (r / 16) * 1024 + (chunk * 16 + r % 16) * 16;
@@ -466,7 +461,7 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_wide_kernel(
             for (int i = 0; i < C::TM; ++i)
 #pragma unroll
                 for (int q4 = 0; q4 < 4; ++q4) {
-                    const int row0 = wm * 64 + i * 32 + 8 * q4 + 4 * (lane / 32);
+                    const int row0 = wm * (32 * C::TM) + i * 32 + 8 * q4 + 4 * (lane / 32);
                     const int4 id4 = *(const int4*)&ids_s[row0];
                     const int32_t ids[4] = {id4.x, id4.y, id4.z, id4.w};
 #pragma unroll
@@ -489,7 +484,7 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_wide_kernel(
             const int blk = ci / kWave, l = ci % kWave;
             const int band = blk / KB, kb = blk % KB;
             const int r = band * 16 + l % 16, chunk = kb * 4 + l / 16;
-            const int col = tn * C::COLS + kb * 32;
+            const int col = col0 + kb * 32;
             const u32x4 v = *(const u32x4*)(stile + (r * CPR + (chunk ^ (r & 15))) * 16);
             if (col < N_out)
                 __builtin_nontemporal_store(
@@ -520,7 +515,7 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_wide_kernel(
             }
             __syncthreads();
             for (int ci = tid; ci < 32 * CPR; ci += C::THREADS) {
-                const int r = ci / CPR, col = tn * C::COLS + (ci % CPR) * (16 / ES);
+                const int r = ci / CPR, col = col0 + (ci % CPR) * (16 / ES);
                 const int32_t id = ids_s[pass * 32 + r];
                 const u32x4 v = *(const u32x4*)(stile + ci * 16);
                 if (real_row(id) && col < N_out)
@@ -529,7 +524,56 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_wide_kernel(
             __syncthreads();
         }
     }
-    __syncthreads();  // the next tile's copies reuse the staging memory
+}
+
+// The persistent grid: the gridDim.x/8 workgroups of an XCD (workgroups go
+// to the 8 XCDs round robin) walk the XCD's contiguous share of the real
+// (row block, N tile) tiles in steps of gridDim.x/8, so at any time they
+// hold consecutive tiles (the row blocks of one expert together) and a
+// workgroup's stores drain while it starts its next tile. When SPLIT and the
+// last round of an XCD holds at most a quarter as many tiles as it has
+// workgroups, those tiles are computed as four quarter-width tiles each
+// (WideQuarterCfg), on four workgroups.
+template <class C, bool Y16, bool SPLIT>
+__global__ __launch_bounds__(C::THREADS) void grouped_gemm_wide_kernel(
+    const uint16_t* __restrict__ a_src, const uint16_t* __restrict__ w, const int32_t* __restrict__ sorted_ids,
+    const int32_t* __restrict__ block_expert, const int32_t* __restrict__ num_padded, int k, int64_t n_pairs,
+    int K, int N_out, int n_tiles, void* __restrict__ out) {
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    const int tid = threadIdx.x, lane = tid % kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // uniform: copy bases and LDS slots in SGPRs
+    const int m_real = *num_padded / C::BM;
+    const int64_t real = (int64_t)m_real * n_tiles;
+    const int64_t share = (real + 7) / 8;
+    const int xcd = blockIdx.x % 8, g = gridDim.x / 8, wg = blockIdx.x / 8;
+    const int64_t t_begin = (int64_t)xcd * share;
+    const int64_t n_x = max((int64_t)0, min(t_begin + share, real) - t_begin);
+    constexpr int QS = SPLIT ? C::BN / WideQuarterCfg<C::BM>::BN : 1;
+    const int64_t rem = n_x % g;
+    const bool split = SPLIT && rem > 0 && rem * QS <= g;
+    const int64_t n_full = split ? n_x - rem : n_x;
+    for (int64_t l = wg; l < n_full; l += g) {
+        const int64_t logical = t_begin + l;
+        const int tn = (int)(logical % n_tiles), mb = (int)(logical / n_tiles);
+        const int e = block_expert[mb];
+        if (e < 0) continue;
+        wide_tile<C, Y16>(a_src, w, sorted_ids, e, mb, tn * (C::BN / 16), tn * C::COLS, k, n_pairs, K, N_out, out,
+                          smem, tid, lane, wave);
+        __syncthreads();  // the next tile's copies reuse the staging memory
+    }
+    if constexpr (SPLIT) {
+        using CQ = WideQuarterCfg<C::BM>;
+        static_assert(!C::GATED && CQ::THREADS == C::THREADS && CQ::BM == C::BM, "quarter tiles of the same block");
+        static_assert(CQ::STAGES * CQ::STAGE_BYTES <= C::STAGES * C::STAGE_BYTES, "quarter tiles fit the stages");
+        if (split && wg < rem * QS) {
+            const int64_t logical = t_begin + n_full + wg / QS;
+            const int sub = wg % QS;
+            const int tn = (int)(logical % n_tiles), mb = (int)(logical / n_tiles);
+            const int e = block_expert[mb];
+            if (e >= 0)
+                wide_tile<CQ, Y16>(a_src, w, sorted_ids, e, mb, tn * (C::BN / 16) + sub * (CQ::BN / 16),
+                                   tn * C::COLS + sub * CQ::COLS, k, n_pairs, K, N_out, out, smem, tid, lane, wave);
+        }
     }
 }
 
@@ -557,10 +601,12 @@ static int launch_wide(const void* a, const void* w, const int32_t* sorted_ids, 
     grid = min(grid, (int64_t)max(8, cus / 8 * 8));
     if (grid >= ((int64_t)1 << 31)) return set_error(MOE_ERR_UNSUPPORTED, "%s: grid too large", what);
     const size_t lds = (size_t)C::STAGES * C::STAGE_BYTES;
+    constexpr bool SPLIT = !C::GATED;  // quarter tiles for the down projection's last round
     static std::atomic<uint64_t> lds_set{0};
-    const int rc = ensure_dynamic_lds((const void*)grouped_gemm_wide_kernel<C, Y16>, (int)lds, lds_set, what);
+    const int rc =
+        ensure_dynamic_lds((const void*)grouped_gemm_wide_kernel<C, Y16, SPLIT>, (int)lds, lds_set, what);
     if (rc) return rc;
-    hipLaunchKernelGGL((grouped_gemm_wide_kernel<C, Y16>), dim3((unsigned)grid), dim3(C::THREADS), lds, s,
+    hipLaunchKernelGGL((grouped_gemm_wide_kernel<C, Y16, SPLIT>), dim3((unsigned)grid), dim3(C::THREADS), lds, s,
                        (const uint16_t*)a, (const uint16_t*)w, sorted_ids, block_expert, num_padded, k, n_pairs, K,
                        N_out, n_tiles, out);
     return check_launch(what);
