@@ -155,10 +155,13 @@ __global__ __launch_bounds__(kAlignThreads) void align_scatter_kernel(
         }
     }
 
-    // Stable scatter of this tile's pairs, 256 per round.
+    // Stable scatter of this tile's pairs, 256 per round; rounds that start
+    // past the last pair (a short single tile) are skipped by the whole
+    // workgroup.
     const unsigned long long below = (1ull << lane) - 1ull;
 #pragma unroll
     for (int q = 0; q < PT; ++q) {
+        if (start + q * kAlignThreads >= n) break;
         const int64_t i = start + q * kAlignThreads + tid;
         const int e = my[q];
         const bool valid = e >= 0;
