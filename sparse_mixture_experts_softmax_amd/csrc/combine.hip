@@ -12,19 +12,20 @@ namespace moe {
 
 constexpr int kCombineThreads = 256;
 
-// Eight consecutive elements of y as fp32.
+// Eight consecutive elements of y as fp32. y is read once, so the loads
+// are non-temporal (skewed and large: 115 -> 101 us).
 template <bool Y16>
 __device__ __forceinline__ void load_y8(const void* y, int64_t idx, float (&v)[8]) {
     if constexpr (Y16) {
-        const u32x4 p = *(const u32x4*)((const _Float16*)y + idx);
+        const u32x4 p = __builtin_nontemporal_load((const u32x4*)((const _Float16*)y + idx));
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             v[2 * q] = (float)__builtin_bit_cast(_Float16, (uint16_t)(p[q] & 0xffffu));
             v[2 * q + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(p[q] >> 16));
         }
     } else {
-        const f32x4 a = *(const f32x4*)((const float*)y + idx);
-        const f32x4 b = *(const f32x4*)((const float*)y + idx + 4);
+        const f32x4 a = __builtin_nontemporal_load((const f32x4*)((const float*)y + idx));
+        const f32x4 b = __builtin_nontemporal_load((const f32x4*)((const float*)y + idx + 4));
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             v[q] = a[q];

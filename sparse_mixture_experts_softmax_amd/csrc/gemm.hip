@@ -120,7 +120,7 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(
     // (sentinel rows, the K tail) are zeroed with sel(). B rows past N_out
     // are clamped to row 0: their columns are never stored.
     u32x4 ra[C::A_PER_T], rb[C::B_PER_T];
-    auto load_tile = [&](int kt) {
+    auto load_tile = [&](int kt, auto once) {
         const int k0 = kt * BK;
 #pragma unroll
         for (int j = 0; j < C::A_PER_T; ++j) {
@@ -133,7 +133,11 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(
         for (int j = 0; j < C::B_PER_T; ++j) {
             const int ks = ((tid + j * C::THREADS) / 64) % C::KS;
             const bool in = kt * C::KS + ks < ksteps;
-            rb[j] = sel(in, ld16(b_ptr[j] + (in ? kt * C::KS * 512 : 0)));
+            const uint16_t* bq = b_ptr[j] + (in ? kt * C::KS * 512 : 0);
+            u32x4 v;
+            if constexpr (decltype(once)::value) v = __builtin_nontemporal_load((const u32x4*)bq);
+            else v = ld16(bq);
+            rb[j] = sel(in, v);
         }
     };
     auto store_tile = [&](int buf) {
@@ -169,29 +173,38 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(
     };
 
     const int nk = (K + BK - 1) / BK;
-    load_tile(0);
-    store_tile(0);
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-        const int buf = kt & 1;
-        if (kt + 1 < nk) load_tile(kt + 1);
-#pragma unroll
-        for (int ks = 0; ks < BK / 32; ++ks) {
-            const int kof = ks * 32 + (lane / 16) * 8;
-            u32x4 fa[C::MT], fb[C::NT];
-#pragma unroll
-            for (int i = 0; i < C::MT; ++i)
-                fa[i] = *(const u32x4*)&sA[buf][(wm * C::WTM + i * 16 + lane % 16) * STRIDE + kof];
-#pragma unroll
-            for (int j = 0; j < C::NT; ++j) fb[j] = *(const u32x4*)&sB[buf][(b_band(j) * C::KS + ks) * 512 + lane * 8];
-#pragma unroll
-            for (int i = 0; i < C::MT; ++i)
-#pragma unroll
-                for (int j = 0; j < C::NT; ++j) acc[i][j] = mfma16x16x32(fa[i], fb[j], acc[i][j]);
-        }
-        if (kt + 1 < nk) store_tile(buf ^ 1);
+    auto run = [&](auto once) {
+        load_tile(0, once);
+        store_tile(0);
         __syncthreads();
-    }
+        for (int kt = 0; kt < nk; ++kt) {
+            const int buf = kt & 1;
+            if (kt + 1 < nk) load_tile(kt + 1, once);
+#pragma unroll
+            for (int ks = 0; ks < BK / 32; ++ks) {
+                const int kof = ks * 32 + (lane / 16) * 8;
+                u32x4 fa[C::MT], fb[C::NT];
+#pragma unroll
+                for (int i = 0; i < C::MT; ++i)
+                    fa[i] = *(const u32x4*)&sA[buf][(wm * C::WTM + i * 16 + lane % 16) * STRIDE + kof];
+#pragma unroll
+                for (int j = 0; j < C::NT; ++j) fb[j] = *(const u32x4*)&sB[buf][(b_band(j) * C::KS + ks) * 512 + lane * 8];
+#pragma unroll
+                for (int i = 0; i < C::MT; ++i)
+#pragma unroll
+                    for (int j = 0; j < C::NT; ++j) acc[i][j] = mfma16x16x32(fa[i], fb[j], acc[i][j]);
+            }
+            if (kt + 1 < nk) store_tile(buf ^ 1);
+            __syncthreads();
+        }
+    };
+    // weights read by no other row block of this launch (the expert's only
+    // block) are loaded non-temporally, as in the skinny kernel
+    const int n_blocks = gridDim.x / n_tiles;
+    if ((mb == 0 || block_expert[mb - 1] != e) && (mb + 1 >= n_blocks || block_expert[mb + 1] != e))
+        run(std::true_type{});
+    else
+        run(std::false_type{});
 
     // Epilogue. Lane holds rows 4*(lane/16)+q, column lane%16 of each 16x16 tile.
     if (C::GATED) {
