@@ -875,12 +875,14 @@ extern "C" int moe_grouped_gemm_down(const void* act, const void* w2, const int3
 
 extern "C" int32_t moe_pick_block_m(int64_t T, int32_t k, int32_t E) {
     if (T < 0 || k < 1 || E < 1) return -1;
-    // 16: weight streaming (skinny kernel); 32: few rows per expert; 128: the
-    // matrix-core bound regime, where the 8-wave 128x512 tile (two waves per
-    // SIMD) beats 64-row blocks despite the extra padding (measured on the
-    // prefill, skewed and large workloads).
+    // 16: weight streaming (skinny kernel), up to 16 rows per expert on
+    // average (at 16 both kernels take the same time on the decode-shaped
+    // layer; at 20, 32-row blocks are 10% faster); 32: few rows per expert;
+    // 128: the matrix-core bound regime, where the 8-wave 128x512 tile (two
+    // waves per SIMD) beats 64-row blocks despite the extra padding (measured
+    // on the prefill, skewed and large workloads).
     const double rows_per_expert = (double)T * k / E;
-    if (rows_per_expert <= 24) return 16;
+    if (rows_per_expert <= 16) return 16;
     if (rows_per_expert <= 64) return 32;
     return 128;
 }
