@@ -407,6 +407,20 @@ def test_block_m_changes_results_only_by_rounding():
         assert np.abs(_f64(o) - ref).max() <= layer_tolerance(ref), bm
 
 
+@pytest.mark.parametrize("T", [40, 150, 600])
+def test_single_and_shared_expert_blocks(T):
+    """Row blocks that are their expert's only one load the weights with a
+    different cache policy from blocks that share an expert: T = 40 gives
+    every expert one 16- or 32-row block, 150 a mix, 600 several per expert.
+    Same values either way: 16- and 32-row blocks agree bit for bit, and
+    both match the oracle."""
+    inp = custom_inputs(f"blocks{T}", T, 256, 16, 4, 128, seed=T)
+    outs = {bm: run_layer(inp, block_m=bm)[0] for bm in (16, 32)}
+    assert np.array_equal(to_bits(outs[16]), to_bits(outs[32]))
+    ref, _, _ = oracle.moe_layer(inp.x, inp.w_router, inp.w13, inp.w2, 4, True)
+    assert np.abs(_f64(outs[16]) - ref).max() <= layer_tolerance(ref)
+
+
 def test_python_errors_on_gpu():
     inp = custom_inputs("err", 8, 64, 8, 2, 32)
     dev = device_inputs(inp)
