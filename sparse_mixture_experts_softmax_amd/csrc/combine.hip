@@ -11,6 +11,7 @@
 namespace moe {
 
 constexpr int kCombineThreads = 256;
+constexpr int kCombineBatch = 8;  // rows of a token loaded together
 
 // Eight consecutive elements of y as fp32. y is read once, so the loads
 // are non-temporal (skewed and large: 115 -> 101 us).
@@ -45,12 +46,28 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const void* __
         float acc[8];
 #pragma unroll
         for (int q = 0; q < 8; ++q) acc[q] = 0.f;
-        for (int j = 0; j < k; ++j) {
-            const float wj = wt[j];
-            float v[8];
-            load_y8<Y16>(y, yt + (int64_t)j * H + h, v);
+        // The k rows are taken kCombineBatch at a time with every load of a
+        // batch issued before any is used (one load per trip of a loop over
+        // k waits for each row in turn). Slots past k re-read row k-1 and
+        // are left out of the sum by a select, so a non-finite y there
+        // cannot reach it; each kept row adds wj * y in row order as before.
+        for (int j0 = 0; j0 < k; j0 += kCombineBatch) {
+            float wj[kCombineBatch], v[kCombineBatch][8];
 #pragma unroll
-            for (int q = 0; q < 8; ++q) acc[q] += wj * v[q];
+            for (int u = 0; u < kCombineBatch; ++u) {
+                const int j = min(j0 + u, k - 1);
+                wj[u] = wt[j];
+                load_y8<Y16>(y, yt + (int64_t)j * H + h, v[u]);
+            }
+#pragma unroll
+            for (int u = 0; u < kCombineBatch; ++u) {
+                const bool use = j0 + u < k;
+#pragma unroll
+                for (int q = 0; q < 8; ++q) {
+                    const float sum = acc[q] + wj[u] * v[u][q];
+                    acc[q] = use ? sum : acc[q];
+                }
+            }
         }
         if (OUT_F32) {
             float* o = (float*)out + t * H + h;

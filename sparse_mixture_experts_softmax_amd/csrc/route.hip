@@ -283,11 +283,14 @@ __global__ __launch_bounds__(kTopkWaves* kWave) void route_topk_kernel(const flo
     const float* row = logits + t * E;
     float v[4];
     uint64_t key[4];
+    // all loads are issued before any is used; keys past E are masked
+    // without a branch (a branch per key made each load wait for the last)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = row[min(lane + i * kWave, E - 1)];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int e = lane + i * kWave;
-        v[i] = row[min(e, E - 1)];
-        key[i] = e < E ? select_key(v[i], e) : 0;
+        key[i] = select_key(v[i], e) & (0ull - (uint64_t)(e < E));
     }
     // k rounds of a wave arg-max; lane j keeps the j-th pick
     int my_id = 0;
@@ -356,11 +359,13 @@ __global__ __launch_bounds__(kTopkWaves* kWave) void route_topk_row_kernel(const
     const float* row = logits + t * E;
     float v[PER];
     uint64_t key[PER];
+    // as above: every load in flight at once, keys past E masked
+#pragma unroll
+    for (int i = 0; i < PER; ++i) v[i] = row[min(r + 16 * i, E - 1)];
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
         const int e = r + 16 * i;
-        v[i] = row[min(e, E - 1)];
-        key[i] = e < E ? select_key(v[i], e) : 0;
+        key[i] = select_key(v[i], e) & (0ull - (uint64_t)(e < E));
     }
     int my_id = 0;
     float my_val = 0.f, mx = 0.f;
