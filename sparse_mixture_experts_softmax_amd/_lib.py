@@ -94,21 +94,51 @@ def _check(rc: int):
         raise MoEError(rc, lib().moe_last_error().decode())
 
 
-def _dev(t: Optional[torch.Tensor], dtype, name: str, optional: bool = False):
+def _dev(t: Optional[torch.Tensor], dtype, name: str, optional: bool = False, numel: int = 0, device=None):
     """data pointer of a contiguous GPU tensor of the given dtype (or None)."""
-    if t is None:
-        if optional:
-            return None
-        raise ValueError(f"{name} is required")
-    if not isinstance(t, torch.Tensor):
-        raise TypeError(f"{name} must be a torch.Tensor")
-    if t.dtype != dtype:
-        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
-    if not t.is_cuda:
-        raise ValueError(f"{name} must be a GPU tensor")
-    if not t.is_contiguous():
-        raise ValueError(f"{name} must be contiguous")
-    return t.data_ptr() if t.numel() else None
+    return _ptrs((t, dtype, name, optional, numel), device=device)[0]
+
+
+def _ptrs(*specs, device=None):
+    """Data pointers of a call's tensors, each spec being (tensor, dtype,
+    name, optional, numel). ``numel`` is the least number of elements the
+    call reads or writes through that tensor (the C ABI takes bare pointers
+    and cannot check sizes, so a short buffer would become an out-of-bounds
+    device access). Every tensor's type, size and layout are checked before
+    any tensor's device, so the checks run the same on a machine without a
+    GPU. All tensors must be on one GPU (``device`` if given)."""
+    for t, dtype, name, optional, numel in specs:
+        if t is None:
+            if optional:
+                continue
+            raise ValueError(f"{name} is required")
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch.Tensor")
+        if t.dtype != dtype:
+            raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+        if t.numel() < numel:
+            raise ValueError(f"{name} has {t.numel()} elements, the call needs at least {numel}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    out = []
+    for t, dtype, name, optional, numel in specs:
+        if t is None:
+            out.append(None)
+            continue
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if device is None:
+            device = t.device
+        elif t.device != device:
+            raise ValueError(f"{name} is on {t.device}, the call's other tensors on {device}")
+        out.append(t.data_ptr() if t.numel() else None)
+    return out
+
+
+def _nonneg(**sizes):
+    for name, v in sizes.items():
+        if int(v) < 0:
+            raise ValueError(f"{name} must be non-negative, got {v}")
 
 
 def _stream(stream, *tensors) -> Optional[int]:
@@ -132,13 +162,14 @@ def moe_route(x, w_router, router_bias, logits, topk_ids, topk_weights, T: int, 
               norm_topk_prob: bool, stream=None):
     """Router linear + softmax + top-k (+ renorm). ``x=None``: logits are an input."""
     bf, f32, i32 = torch.bfloat16, torch.float32, torch.int32
-    args = (
-        _dev(x, bf, "x", optional=True),
-        _dev(w_router, bf, "w_router", optional=x is None),
-        _dev(router_bias, f32, "router_bias", optional=True),
-        _dev(logits, f32, "logits"),
-        _dev(topk_ids, i32, "topk_ids"),
-        _dev(topk_weights, f32, "topk_weights"),
+    _nonneg(T=T, H=H, E=E, k=k)
+    args = _ptrs(
+        (x, bf, "x", True, T * H),
+        (w_router, bf, "w_router", x is None, E * H if x is not None else 0),
+        (router_bias, f32, "router_bias", True, E),
+        (logits, f32, "logits", False, T * E),
+        (topk_ids, i32, "topk_ids", False, T * k),
+        (topk_weights, f32, "topk_weights", False, T * k),
     )
     _check(lib().moe_route(*args, T, H, E, k, int(bool(norm_topk_prob)), _stream(stream, logits)))
 
@@ -162,39 +193,48 @@ def moe_packed_weight_bytes(E: int, N: int, K: int) -> int:
 def moe_pack_weights(w, w_packed, E: int, N: int, K: int, gated: bool, stream=None):
     """Row-major [E, N, K] bf16 -> the GEMMs' fragment layout (same size)."""
     bf = torch.bfloat16
-    _check(lib().moe_pack_weights(_dev(w, bf, "w"), _dev(w_packed, bf, "w_packed"), E, N, K, int(bool(gated)),
-                                  _stream(stream, w)))
+    _nonneg(E=E, N=N, K=K)
+    pw, pp = _ptrs((w, bf, "w", False, E * N * K), (w_packed, bf, "w_packed", False, E * N * K))
+    _check(lib().moe_pack_weights(pw, pp, E, N, K, int(bool(gated)), _stream(stream, w)))
 
 
 def moe_fused_add_rmsnorm(x, residual, weight, T: int, H: int, eps: float, has_residual: bool, stream=None):
     """In place: residual <- residual + x (or x), x <- rmsnorm(residual)."""
     bf = torch.bfloat16
-    _check(lib().moe_fused_add_rmsnorm(_dev(x, bf, "x"), _dev(residual, bf, "residual"), _dev(weight, bf, "weight"),
-                                       T, H, float(eps), int(bool(has_residual)), _stream(stream, x)))
+    _nonneg(T=T, H=H)
+    px, pr, pw = _ptrs((x, bf, "x", False, T * H), (residual, bf, "residual", False, T * H),
+                       (weight, bf, "weight", False, H))
+    _check(lib().moe_fused_add_rmsnorm(px, pr, pw, T, H, float(eps), int(bool(has_residual)), _stream(stream, x)))
 
 
 def moe_align_by_expert(topk_ids, T: int, k: int, E: int, block_m: int, sorted_ids, block_expert, expert_counts,
                         num_padded, workspace=None, stream=None):
     i32 = torch.int32
-    ws_ptr, ws_bytes = None, 0
+    _nonneg(T=T, k=k, E=E)
+    cap = max(0, lib().moe_align_capacity(T, k, E, block_m))
+    ws_bytes = 0
     if workspace is not None:
-        if not workspace.is_cuda or not workspace.is_contiguous():
-            raise ValueError("workspace must be a contiguous GPU tensor")
-        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
-    _check(lib().moe_align_by_expert(_dev(topk_ids, i32, "topk_ids"), T, k, E, block_m,
-                                     _dev(sorted_ids, i32, "sorted_ids"), _dev(block_expert, i32, "block_expert"),
-                                     _dev(expert_counts, i32, "expert_counts"), _dev(num_padded, i32, "num_padded"),
-                                     ws_ptr, ws_bytes, _stream(stream, topk_ids)))
+        if not isinstance(workspace, torch.Tensor):
+            raise TypeError("workspace must be a torch.Tensor")
+        ws_bytes = workspace.numel() * workspace.element_size()
+    p = _ptrs((topk_ids, i32, "topk_ids", False, T * k), (sorted_ids, i32, "sorted_ids", False, cap),
+              (block_expert, i32, "block_expert", False, cap // max(block_m, 1)),
+              (expert_counts, i32, "expert_counts", False, E), (num_padded, i32, "num_padded", False, 1),
+              (workspace, workspace.dtype if workspace is not None else None, "workspace", True, 0))
+    _check(lib().moe_align_by_expert(p[0], T, k, E, block_m, p[1], p[2], p[3], p[4], p[5], ws_bytes,
+                                     _stream(stream, topk_ids)))
 
 
 def moe_grouped_gemm_gate_up_silu(x, w13, sorted_ids, block_expert, num_padded, T: int, k: int, H: int, I: int,
                                   E: int, block_m: int, cap: int, act, stream=None):
     bf, i32 = torch.bfloat16, torch.int32
-    _check(lib().moe_grouped_gemm_gate_up_silu(_dev(x, bf, "x"), _dev(w13, bf, "w13"),
-                                               _dev(sorted_ids, i32, "sorted_ids"),
-                                               _dev(block_expert, i32, "block_expert"),
-                                               _dev(num_padded, i32, "num_padded"), T, k, H, I, E, block_m, cap,
-                                               _dev(act, bf, "act"), _stream(stream, x)))
+    _nonneg(T=T, k=k, H=H, I=I, E=E, cap=cap)
+    bm = max(block_m, 1)
+    p = _ptrs((x, bf, "x", False, T * H), (w13, bf, "w13", False, E * 2 * I * H),
+              (sorted_ids, i32, "sorted_ids", False, cap), (block_expert, i32, "block_expert", False, cap // bm),
+              (num_padded, i32, "num_padded", False, 1), (act, bf, "act", False, cap * I))
+    _check(lib().moe_grouped_gemm_gate_up_silu(p[0], p[1], p[2], p[3], p[4], T, k, H, I, E, block_m, cap, p[5],
+                                               _stream(stream, x)))
 
 
 def _y_dtype(y) -> int:
@@ -208,9 +248,12 @@ def moe_grouped_gemm_down(act, w2, sorted_ids, block_expert, num_padded, T: int,
     """``y`` dtype (fp16 or fp32) selects the stored precision of y."""
     bf, i32 = torch.bfloat16, torch.int32
     yd = _y_dtype(y)
-    _check(lib().moe_grouped_gemm_down(_dev(act, bf, "act"), _dev(w2, bf, "w2"), _dev(sorted_ids, i32, "sorted_ids"),
-                                       _dev(block_expert, i32, "block_expert"), _dev(num_padded, i32, "num_padded"),
-                                       T, k, H, I, E, block_m, cap, _dev(y, y.dtype, "y"), yd,
+    _nonneg(T=T, k=k, H=H, I=I, E=E, cap=cap)
+    bm = max(block_m, 1)
+    p = _ptrs((act, bf, "act", False, cap * I), (w2, bf, "w2", False, E * H * I),
+              (sorted_ids, i32, "sorted_ids", False, cap), (block_expert, i32, "block_expert", False, cap // bm),
+              (num_padded, i32, "num_padded", False, 1), (y, y.dtype, "y", False, T * k * H))
+    _check(lib().moe_grouped_gemm_down(p[0], p[1], p[2], p[3], p[4], T, k, H, I, E, block_m, cap, p[5], yd,
                                        _stream(stream, act)))
 
 
@@ -221,5 +264,7 @@ def moe_combine(y, topk_weights, T: int, k: int, H: int, out, stream=None):
         raise TypeError("out must be a bf16 or fp32 tensor")
     od = MOE_OUT_FP32 if out.dtype == torch.float32 else MOE_OUT_BF16
     yd = _y_dtype(y)
-    _check(lib().moe_combine(_dev(y, y.dtype, "y"), yd, _dev(topk_weights, torch.float32, "topk_weights"), T, k, H,
-                             _dev(out, out.dtype, "out"), od, _stream(stream, y)))
+    _nonneg(T=T, k=k, H=H)
+    p = _ptrs((y, y.dtype, "y", False, T * k * H), (topk_weights, torch.float32, "topk_weights", False, T * k),
+              (out, out.dtype, "out", False, T * H))
+    _check(lib().moe_combine(p[0], yd, p[1], T, k, H, p[2], od, _stream(stream, y)))

@@ -118,7 +118,11 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(
 
     // Unconditional loads from clamped addresses; values outside the operand
     // (sentinel rows, the K tail) are zeroed with sel(). B rows past N_out
-    // are clamped to row 0: their columns are never stored.
+    // are clamped to row 0: their columns are never stored. When K % 64 ==
+    // 32 the second half of the last K tile lies past the operand: those
+    // chunks load from k-step 0 of the same row or band instead (a_ptr and
+    // b_ptr already include the chunk's k-step offset within the tile, which
+    // there points past the row band or the weight), and sel() drops them.
     u32x4 ra[C::A_PER_T], rb[C::B_PER_T];
     auto load_tile = [&](int kt, auto once) {
         const int k0 = kt * BK;
@@ -126,14 +130,18 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(
         for (int j = 0; j < C::A_PER_T; ++j) {
             const int kc = ((tid + j * C::THREADS) % (BK / 8)) * 8;
             const bool in = k0 + kc < K;
-            // act fragments: columns k0.. of a row sit k0 / 32 blocks of 512 on
-            ra[j] = sel(a_ok[j] && in, ld16(a_ptr[j] + (in ? (C::GATED ? k0 : k0 * 16) : 0)));
+            // gathered x rows: columns k0.. are k0 elements on (K = H is a
+            // multiple of 64, so always in); act fragments: columns k0.. of a
+            // row sit k0 / 32 blocks of 512 on, and column kc itself (kc / 32)
+            // blocks on, which is undone when out of range
+            const int64_t off = C::GATED ? (in ? k0 : 0) : (in ? (int64_t)k0 * 16 : -(int64_t)(kc >> 5) * 512);
+            ra[j] = sel(a_ok[j] && in, ld16(a_ptr[j] + off));
         }
 #pragma unroll
         for (int j = 0; j < C::B_PER_T; ++j) {
             const int ks = ((tid + j * C::THREADS) / 64) % C::KS;
             const bool in = kt * C::KS + ks < ksteps;
-            const uint16_t* bq = b_ptr[j] + (in ? kt * C::KS * 512 : 0);
+            const uint16_t* bq = b_ptr[j] + (in ? (int64_t)kt * C::KS * 512 : -(int64_t)ks * 512);
             u32x4 v;
             if constexpr (decltype(once)::value) v = __builtin_nontemporal_load((const u32x4*)bq);
             else v = ld16(bq);

@@ -102,6 +102,31 @@ def allocate(T: int, H: int, E: int, k: int, I: int, device, block_m: Optional[i
     )
 
 
+def check_buffers(b: MoEBuffers, T: int, H: int, E: int, k: int, I: int, device) -> None:
+    """Raise ValueError unless ``b`` was allocated for this call's (T, H, E,
+    k, I) on ``device`` (a buffer from another shape would be written out of
+    bounds by the kernels, which take bare pointers)."""
+    cap = _lib.moe_align_capacity(T, k, E, b.block_m)
+    if cap < 0 or b.cap != cap:
+        raise ValueError(f"buffers hold cap={b.cap} rows, the call needs moe_align_capacity(T={T}, k={k}, E={E}, "
+                         f"block_m={b.block_m}) = {cap}")
+    want = {
+        "logits": (T, E), "topk_ids": (T, k), "topk_weights": (T, k), "sorted_ids": (cap,),
+        "block_expert": (cap // b.block_m,), "expert_counts": (E,), "num_padded": (1,), "act": (cap, I),
+        "y": (T * k, H), "out": (T, H),
+    }
+    for name, shape in want.items():
+        t = getattr(b, name)
+        if tuple(t.shape) != shape:
+            raise ValueError(f"buffers.{name} has shape {tuple(t.shape)}, the call needs {shape}")
+        if t.device != torch.device(device):
+            raise ValueError(f"buffers.{name} is on {t.device}, x on {device}")
+    ws = _lib.moe_align_workspace_bytes(T, k, E, b.block_m)
+    have = 0 if b.workspace is None else b.workspace.numel() * b.workspace.element_size()
+    if have < ws:
+        raise ValueError(f"buffers.workspace holds {have} bytes, the call needs {ws}")
+
+
 def moe_layer(x: torch.Tensor, w_router: torch.Tensor, w13: Optional[torch.Tensor] = None,
               w2: Optional[torch.Tensor] = None, *, top_k: int, norm_topk_prob: bool = True,
               router_bias: Optional[torch.Tensor] = None, packed: Optional[PackedExperts] = None,
@@ -133,7 +158,14 @@ def moe_layer(x: torch.Tensor, w_router: torch.Tensor, w13: Optional[torch.Tenso
                          f"experts E={packed.num_experts} H={packed.hidden_size} I={I}")
     w13p, w2p = packed.w13, packed.w2
     k = int(top_k)
-    b = buffers if buffers is not None else allocate(T, H, E, k, I, x.device, block_m, out_dtype, y_dtype)
+    for name, t in (("w_router", w_router), ("router_bias", router_bias), ("packed w13", w13p), ("packed w2", w2p)):
+        if t is not None and t.device != x.device:
+            raise ValueError(f"{name} is on {t.device}, x on {x.device}")
+    if buffers is not None:
+        check_buffers(buffers, T, H, E, k, I, x.device)
+        b = buffers
+    else:
+        b = allocate(T, H, E, k, I, x.device, block_m, out_dtype, y_dtype)
     s = _lib._stream(stream, x)
     _lib.moe_route(x, w_router, router_bias, b.logits, b.topk_ids, b.topk_weights, T, H, E, k, norm_topk_prob, s)
     _lib.moe_align_by_expert(b.topk_ids, T, k, E, b.block_m, b.sorted_ids, b.block_expert, b.expert_counts,

@@ -189,3 +189,89 @@ def test_build_rejects_scratch():
                      "a.hip:9:1: remark:     ScratchSize [bytes/lane]: 36 [-Rpass-analysis=kernel-resource-usage]\n")
     assert build._scratch_users(clean) == []
     assert build._scratch_users(spill) == ["_Z1jv (36 bytes/lane)"]
+
+
+# ----------------------------------------------------------------------------
+# The Python binding checks buffer sizes before anything reaches the C ABI
+# (which takes bare pointers and cannot): a short buffer raises ValueError.
+# ----------------------------------------------------------------------------
+def _t(n, dtype=torch.int32):
+    return torch.zeros(n, dtype=dtype)
+
+
+@pytest.mark.parametrize("which", ["topk_ids", "sorted_ids", "block_expert", "expert_counts", "num_padded"])
+def test_align_binding_rejects_short_buffers(which):
+    T, k, E, bm = 100, 4, 16, 32
+    cap = moe.moe_align_capacity(T, k, E, bm)
+    bufs = dict(topk_ids=_t(T * k), sorted_ids=_t(cap), block_expert=_t(cap // bm), expert_counts=_t(E),
+                num_padded=_t(1))
+    bufs[which] = _t(bufs[which].numel() - 1)
+    with pytest.raises(ValueError, match=which):
+        moe.moe_align_by_expert(bufs["topk_ids"], T, k, E, bm, bufs["sorted_ids"], bufs["block_expert"],
+                                bufs["expert_counts"], bufs["num_padded"])
+
+
+@pytest.mark.parametrize("which", ["x", "w_router", "logits", "topk_ids", "topk_weights"])
+def test_route_binding_rejects_short_buffers(which):
+    T, H, E, k = 10, 64, 8, 2
+    bf, f32 = torch.bfloat16, torch.float32
+    bufs = dict(x=_t(T * H, bf), w_router=_t(E * H, bf), logits=_t(T * E, f32), topk_ids=_t(T * k),
+                topk_weights=_t(T * k, f32))
+    bufs[which] = _t(bufs[which].numel() - 1, bufs[which].dtype)
+    with pytest.raises(ValueError, match=which):
+        moe.moe_route(bufs["x"], bufs["w_router"], None, bufs["logits"], bufs["topk_ids"], bufs["topk_weights"], T, H,
+                      E, k, True)
+
+
+@pytest.mark.parametrize("which", ["x", "w13", "sorted_ids", "block_expert", "act"])
+def test_gate_up_binding_rejects_short_buffers(which):
+    T, H, E, k, I, bm = 10, 64, 8, 2, 32, 16
+    cap = moe.moe_align_capacity(T, k, E, bm)
+    bf = torch.bfloat16
+    bufs = dict(x=_t(T * H, bf), w13=_t(E * 2 * I * H, bf), sorted_ids=_t(cap), block_expert=_t(cap // bm),
+                num_padded=_t(1), act=_t(cap * I, bf))
+    bufs[which] = _t(bufs[which].numel() - 1, bufs[which].dtype)
+    with pytest.raises(ValueError, match=which):
+        moe.moe_grouped_gemm_gate_up_silu(bufs["x"], bufs["w13"], bufs["sorted_ids"], bufs["block_expert"],
+                                          bufs["num_padded"], T, k, H, I, E, bm, cap, bufs["act"])
+
+
+@pytest.mark.parametrize("which", ["act", "w2", "y"])
+def test_down_and_combine_bindings_reject_short_buffers(which):
+    T, H, E, k, I, bm = 10, 64, 8, 2, 32, 16
+    cap = moe.moe_align_capacity(T, k, E, bm)
+    bf = torch.bfloat16
+    bufs = dict(act=_t(cap * I, bf), w2=_t(E * H * I, bf), y=_t(T * k * H, torch.float16))
+    bufs[which] = _t(bufs[which].numel() - 1, bufs[which].dtype)
+    with pytest.raises(ValueError, match=which):
+        moe.moe_grouped_gemm_down(bufs["act"], bufs["w2"], _t(cap), _t(cap // bm), _t(1), T, k, H, I, E, bm, cap,
+                                  bufs["y"])
+    if which == "y":
+        with pytest.raises(ValueError, match="y"):
+            moe.moe_combine(bufs["y"], _t(T * k, torch.float32), T, k, H, _t(T * H, bf))
+    with pytest.raises(ValueError, match="out"):
+        moe.moe_combine(_t(T * k * H, torch.float16), _t(T * k, torch.float32), T, k, H, _t(T * H - 8, bf))
+
+
+def test_layer_rejects_buffers_of_another_shape():
+    """Buffers allocated for one (T, k, E, block_m) cannot be reused for a call
+    whose capacity or shapes differ."""
+    from sparse_mixture_experts_softmax_amd.layer import check_buffers
+
+    b = moe.allocate(64, 128, 8, 2, 64, "cpu", block_m=16)
+    check_buffers(b, 64, 128, 8, 2, 64, "cpu")  # the shape it was made for
+    with pytest.raises(ValueError, match="cap|logits"):
+        check_buffers(b, 65, 128, 8, 2, 64, "cpu")
+    with pytest.raises(ValueError, match="cap"):
+        check_buffers(b, 200, 128, 8, 2, 64, "cpu")
+    with pytest.raises(ValueError, match="act"):
+        check_buffers(b, 64, 128, 8, 2, 96, "cpu")
+    with pytest.raises(ValueError, match="out|y"):
+        check_buffers(b, 64, 192, 8, 2, 64, "cpu")
+    with pytest.raises(ValueError, match="cap|logits"):
+        check_buffers(b, 64, 128, 9, 2, 64, "cpu")
+
+
+def test_binding_rejects_negative_sizes():
+    with pytest.raises(ValueError, match="non-negative"):
+        moe.moe_combine(_t(8, torch.float16), _t(1, torch.float32), -1, 1, 64, _t(64, torch.bfloat16))

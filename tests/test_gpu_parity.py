@@ -6,6 +6,10 @@ the oracle step they implement, fed the GPU's own upstream intermediate;
 the whole layer is compared with the oracle on all five workloads within
 max|err| <= 2e-2 * rms(out) + 1e-3 (and, on the tiny workload, also without
 the 1e-3 floor)."""
+import dataclasses
+import functools
+import time
+
 import numpy as np
 import pytest
 import torch
@@ -212,8 +216,28 @@ def test_pack_weights_matches_layout_definition(E, N, K, gated):
 F16, F32 = torch.float16, torch.float32
 
 
+def rows_covering_every_block(sorted_ids, npad, bm, n_pairs, seed=0):
+    """Real rows of the permutation to check: all of them for small cases;
+    otherwise, in every row block, the first and the last real row and one
+    seeded random real row, so every (row block, column tile) of both GEMMs
+    (each expert's last, partly padded block included) has checked rows."""
+    real = np.nonzero(sorted_ids[:npad] != n_pairs)[0]
+    if real.size <= 256:
+        return real
+    rng = np.random.default_rng(seed)
+    pick = []
+    blocks = real // bm
+    starts = np.searchsorted(blocks, np.arange(npad // bm))
+    ends = np.searchsorted(blocks, np.arange(npad // bm), side="right")
+    for lo, hi in zip(starts, ends):
+        if hi > lo:
+            pick += [real[lo], real[hi - 1], real[rng.integers(lo, hi)]]
+    return np.unique(np.array(pick))
+
+
 @pytest.mark.parametrize("name,y_dtype", [("tiny", F16), ("tiny", F32), ("decode", F16), ("decode", F32),
-                                          ("prefill", F16), ("prefill", F32), ("large", F16)])
+                                          ("prefill", F16), ("prefill", F32), ("skewed", F16), ("skewed", F32),
+                                          ("large", F16)])
 def test_gemms_and_combine_against_oracle_steps(name, y_dtype):
     log(f"steps {name} y {y_dtype}")
     inp = host_inputs(name)
@@ -225,61 +249,81 @@ def test_gemms_and_combine_against_oracle_steps(name, y_dtype):
     block_expert = b.block_expert.cpu().numpy()
     npad = int(b.num_padded.item())
     n = s.T * s.k
-    rows = np.nonzero(sorted_ids[:npad] != n)[0]
+    rows = rows_covering_every_block(sorted_ids, npad, b.block_m, n)
     pads = np.nonzero(sorted_ids[:npad] == n)[0]
-    rng = np.random.default_rng(0)
-    if rows.size > 192:
-        rows = np.sort(rng.choice(rows, 192, replace=False))
+    blocks_checked = np.unique(rows // b.block_m).size
+    blocks_real = np.unique(np.nonzero(sorted_ids[:npad] != n)[0] // b.block_m).size
+    log(f"  {rows.size} rows checked, covering {blocks_checked} of {blocks_real} row blocks")
+    assert blocks_checked == blocks_real
     act = act_rows(b.act)
     # pad rows of act are zero
     if pads.size:
         assert not _f64(act[torch.from_numpy(pads).cuda()]).any()
     x64 = synth.bf16_to_f64(inp.x)
     act_ref, act_gpu, y_ref, y_gpu = [], [], [], []
-    for r in rows:
+    act_sel = _f64(act[torch.from_numpy(rows).cuda()])
+    y_sel = _f64(b.y[torch.from_numpy(sorted_ids[rows].astype(np.int64)).cuda()])
+    for q, r in enumerate(rows):
         i = int(sorted_ids[r])
         t, e = i // s.k, int(block_expert[r // b.block_m])
         act_ref.append(oracle.expert_gate_up(x64[t], inp.w13[e])[0])
-        a_gpu = _f64(act[r])
+        a_gpu = act_sel[q]
         act_gpu.append(a_gpu)
         y_ref.append(oracle.expert_down(a_gpu, inp.w2[e])[0])
-        y_gpu.append(_f64(b.y[i]))
+        y_gpu.append(y_sel[q])
     elem_close(np.array(act_gpu), np.array(act_ref), what="gate_up act")
     # fp32 accumulation error (far below the floor), plus the rounding of the
     # stored y: half an fp16 ulp (2^-11 relative; fp16 subnormals, below
     # 6.1e-5, are far below the floor)
     rel = 1e-5 + (2.0 ** -11 if y_dtype == F16 else 0.0)
     elem_close(np.array(y_gpu), np.array(y_ref), rel=rel, floor_frac=1e-4, what="down y")
-    # combine: fp32 output against the oracle's weighted sum of the GPU's y
-    toks = sample_tokens(s.T, 128)
+    # combine, every token: fp32 output against the oracle's weighted sum of
+    # the GPU's y (in chunks of tokens to bound host memory)
     out32 = torch.empty((s.T, s.H), dtype=torch.float32, device="cuda")
     moe.moe_combine(b.y, b.topk_weights, s.T, s.k, s.H, out32)
     torch.cuda.synchronize()
-    y3 = _f64(b.y).reshape(s.T, s.k, s.H)[toks]
-    w3 = b.topk_weights.cpu().numpy().astype(np.float64)[toks]
-    ref = oracle.combine(y3, w3)
-    tol = (s.k + 1) * 2.0 ** -23 * (np.abs(w3)[:, :, None] * np.abs(y3)).sum(1) + 1e-30  # fp32 sum of k products
-    assert (np.abs(out32.cpu().numpy()[toks] - ref) <= tol).all()
-    elem_close(_f64(out)[toks], ref, rel=2.0 ** -8, floor_frac=1e-6, what="combine bf16")
+    w_all = b.topk_weights.cpu().numpy().astype(np.float64)
+    for t0 in range(0, s.T, 1024):
+        t1 = min(s.T, t0 + 1024)
+        y3 = _f64(b.y[t0 * s.k:t1 * s.k]).reshape(t1 - t0, s.k, s.H)
+        w3 = w_all[t0:t1]
+        ref = oracle.combine(y3, w3)
+        tol = (s.k + 1) * 2.0 ** -23 * (np.abs(w3)[:, :, None] * np.abs(y3)).sum(1) + 1e-30  # fp32 sum of k products
+        assert (np.abs(_f64(out32[t0:t1]) - ref) <= tol).all(), f"combine fp32, tokens {t0}..{t1}"
+        elem_close(_f64(out[t0:t1]), ref, rel=2.0 ** -8, floor_frac=1e-6, what=f"combine bf16, tokens {t0}..{t1}")
 
 
 # ----------------------------------------------------------------------------
 # The whole layer
 # ----------------------------------------------------------------------------
+@functools.lru_cache(maxsize=1)
+def oracle_layer_all_tokens(name):
+    """The oracle's output for every token of a workload (cached: the fp64
+    per-token loop takes seconds to tens of seconds at the large shapes)."""
+    inp = host_inputs(name)
+    s = inp.shape
+    t0 = time.perf_counter()
+    ref = oracle.moe_layer(inp.x, inp.w_router, inp.w13, inp.w2, s.k, s.norm_topk_prob, inp.router_bias)
+    log(f"  oracle: {s.T} tokens of {name} in {time.perf_counter() - t0:.1f} s "
+        f"({oracle.default().max_threads()} threads)")
+    return ref
+
+
 @pytest.mark.parametrize("name,y_dtype", [(n, F16) for n in CONFIG_NAMES] + [("tiny", F32), ("large", F32)])
 def test_layer_matches_oracle(name, y_dtype):
+    """Every token of every workload (so every row block and column tile of
+    both GEMMs) against the oracle."""
     log(f"layer {name} y {y_dtype}")
     inp = host_inputs(name)
     s = inp.shape
     dev = device_inputs(inp, key=name)
     out, b = run_layer(inp, dev, y_dtype=y_dtype)
-    toks = sample_tokens(s.T, 96)
-    ref, ref_ids, ref_w = oracle.moe_layer(inp.x, inp.w_router, inp.w13, inp.w2, s.k, s.norm_topk_prob,
-                                           inp.router_bias, toks)
-    got = _f64(out)[toks]
+    ref, ref_ids, ref_w = oracle_layer_all_tokens(name)
+    got = _f64(out)
+    assert got.shape == ref.shape
     assert np.isfinite(got).all()
-    assert np.array_equal(b.topk_ids.cpu().numpy()[toks], ref_ids)
-    assert np.abs(b.topk_weights.cpu().numpy()[toks] - ref_w).max() <= 1e-6
+    assert np.array_equal(b.topk_ids.cpu().numpy(), ref_ids)
+    assert np.abs(b.topk_weights.cpu().numpy() - ref_w).max() <= 1e-6
     err = np.abs(got - ref).max()
     tol = layer_tolerance(ref)
     log(f"  {name}: max err {err:.3e}, bound {tol:.3e}, rms {np.sqrt(np.mean(ref ** 2)):.3e}")
@@ -313,13 +357,60 @@ def test_layer_edge_cases():
 
 
 def test_zero_tokens_is_a_noop():
+    """T = 0: every entry point returns success and writes nothing. Each call
+    gets real, sentinel-filled buffers (sized for T = 4) and they must come
+    back unchanged; the layer returns an empty [0, H] output."""
     inp = custom_inputs("empty", 4, 64, 8, 2, 32)
     dev = device_inputs(inp)
-    out = torch.full((0, 64), 3.0, dtype=torch.bfloat16, device="cuda")
-    x0 = dev["x"][:0]
-    res = moe.moe_layer(x0, dev["w_router"], top_k=2, packed=dev["packed"])
+    b = moe.allocate(4, 64, 8, 2, 32, "cuda", block_m=16)
+    for name in ("logits", "topk_weights", "act", "y", "out"):
+        getattr(b, name).fill_(3.0)
+    for name in ("topk_ids", "sorted_ids", "block_expert", "expert_counts", "num_padded"):
+        getattr(b, name).fill_(-5)
+    before = {f.name: getattr(b, f.name).clone() for f in dataclasses.fields(b)
+              if isinstance(getattr(b, f.name), torch.Tensor)}
+    x, pk = dev["x"], dev["packed"]
+    moe.moe_route(x, dev["w_router"], None, b.logits, b.topk_ids, b.topk_weights, 0, 64, 8, 2, True)
+    moe.moe_route(None, None, None, b.logits, b.topk_ids, b.topk_weights, 0, 0, 8, 2, True)
+    moe.moe_align_by_expert(b.topk_ids, 0, 2, 8, 16, b.sorted_ids, b.block_expert, b.expert_counts, b.num_padded)
+    moe.moe_grouped_gemm_gate_up_silu(x, pk.w13, b.sorted_ids, b.block_expert, b.num_padded, 0, 2, 64, 32, 8, 16,
+                                      0, b.act)
+    moe.moe_grouped_gemm_down(b.act, pk.w2, b.sorted_ids, b.block_expert, b.num_padded, 0, 2, 64, 32, 8, 16, 0, b.y)
+    moe.moe_combine(b.y, b.topk_weights, 0, 2, 64, b.out)
     torch.cuda.synchronize()
-    assert res.shape == (0, 64) and out.shape == (0, 64)
+    for name, t in before.items():
+        assert torch.equal(getattr(b, name), t), f"{name} was written by a T = 0 call"
+    res = moe.moe_layer(x[:0], dev["w_router"], top_k=2, packed=pk)
+    torch.cuda.synchronize()
+    assert res.shape == (0, 64) and res.dtype == torch.bfloat16 and res.device == x.device
+
+
+@pytest.mark.parametrize("bm", [16, 32, 128])
+def test_expert_outputs_beyond_fp16_range(bm):
+    """Expert outputs far beyond +-65504 (the down weights scaled by 2^23,
+    exact in bf16). With fp32 y the layer still matches the oracle; with fp16
+    y an output element is non-finite exactly where one of its token's k
+    expert outputs rounds past the fp16 range (|y| >= 65520, judged on the
+    fp32 y of the same run), and finite and unchanged elsewhere."""
+    base = custom_inputs(f"bigy{bm}", 160, 256, 8, 2, 128, seed=21)
+    s = base.shape
+    w2 = (synth.bf16_to_f64(base.w2) * 2.0 ** 23).astype(np.float32)
+    w2_bits = (w2.view(np.uint32) >> 16).astype(np.uint16)  # exact: a power-of-two scale of bf16 values
+    inp = synth.MoEInputs(s, base.seed, base.x, base.w_router, base.w13, w2_bits, None)
+    o32, b32 = run_layer(inp, block_m=bm, y_dtype=F32)
+    o16, b16 = run_layer(inp, block_m=bm, y_dtype=F16)
+    ref, _, _ = oracle.moe_layer(inp.x, inp.w_router, inp.w13, inp.w2, s.k, s.norm_topk_prob)
+    y32 = _f64(b32.y).reshape(s.T, s.k, s.H)
+    assert np.abs(y32).max() > 1e5  # the case is real
+    got32 = _f64(o32)
+    assert np.isfinite(got32).all()
+    assert np.abs(got32 - ref).max() <= layer_tolerance(ref)
+    over = (np.abs(y32) >= 65520.0).any(axis=1)
+    got16 = _f64(o16)
+    assert np.array_equal(~np.isfinite(got16), over)
+    assert over.any() and (~over).any()
+    fin = ~over
+    assert np.abs(got16[fin] - ref[fin]).max() <= layer_tolerance(ref)
 
 
 # ----------------------------------------------------------------------------
@@ -355,7 +446,7 @@ def test_nan_poison_unused_experts_and_pad_rows():
     assert np.array_equal(to_bits(out2), to_bits(clean))
 
 
-@pytest.mark.parametrize("name", ["decode", "prefill"])
+@pytest.mark.parametrize("name", ["decode", "prefill", "skewed", "large"])
 def test_run_twice_bit_identical(name):
     inp = host_inputs(name)
     dev = device_inputs(inp, key=name)
@@ -371,15 +462,16 @@ def test_run_twice_bit_identical(name):
     assert np.array_equal(to_bits(o1), to_bits(o2))
 
 
-def test_batch_split_bit_identical():
+@pytest.mark.parametrize("bm", [64, 128])
+def test_batch_split_bit_identical(bm):
     inp = host_inputs("prefill")
     s = inp.shape
     dev = device_inputs(inp, key="prefill")
-    full, _ = run_layer(inp, dev, block_m=64)
+    full, _ = run_layer(inp, dev, block_m=bm)
     half = s.T // 2
     sub = synth.MoEInputs(s.with_tokens(half), 0, inp.x[:half], inp.w_router, inp.w13, inp.w2, inp.router_bias)
     dsub = dict(dev, x=dev["x"][:half].contiguous())
-    part, _ = run_layer(sub, dsub, block_m=64)
+    part, _ = run_layer(sub, dsub, block_m=bm)
     assert np.array_equal(to_bits(part), to_bits(full[:half]))
 
 
