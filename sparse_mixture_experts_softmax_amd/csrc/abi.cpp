@@ -49,7 +49,9 @@ int device_cu_count(const char* what) {
     return n;
 }
 
-bool valid_block_m(int32_t block_m) { return block_m == 16 || block_m == 32 || block_m == 64 || block_m == 128; }
+bool valid_block_m(int32_t block_m) {
+    return block_m == 16 || block_m == 32 || block_m == 64 || block_m == 128 || block_m == 256;
+}
 
 int check_shape(const char* fn, int64_t T, int32_t H, int32_t E, int32_t k, int32_t I) {
     if (T < 0 || H < 0 || E < 0 || k < 0) return set_error(MOE_ERR_INVALID, "%s: negative size", fn);

@@ -555,7 +555,11 @@ __device__ __forceinline__ void wide_tile(const uint16_t* __restrict__ a_src, co
 // last round of an XCD holds at most a quarter as many tiles as it has
 // workgroups, those tiles are computed as four quarter-width tiles each
 // (WideQuarterCfg), on four workgroups.
-template <class C, bool Y16, bool SPLIT>
+//
+// AM: grouping blocks per tile row block. With block_m 256 the grouping pads
+// each expert to 256 rows and every 256-row block is computed as two 128-row
+// tiles (AM = 2) of the same expert, so the row block of tile mb is mb / AM.
+template <class C, bool Y16, bool SPLIT, int AM = 1>
 __global__ __launch_bounds__(C::THREADS) void grouped_gemm_wide_kernel(
     const uint16_t* __restrict__ a_src, const uint16_t* __restrict__ w, const int32_t* __restrict__ sorted_ids,
     const int32_t* __restrict__ block_expert, const int32_t* __restrict__ num_padded, int k, int64_t n_pairs,
@@ -576,7 +580,7 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_wide_kernel(
     for (int64_t l = wg; l < n_full; l += g) {
         const int64_t logical = t_begin + l;
         const int tn = (int)(logical % n_tiles), mb = (int)(logical / n_tiles);
-        const int e = block_expert[mb];
+        const int e = block_expert[mb / AM];
         if (e < 0) continue;
         wide_tile<C, Y16>(a_src, w, sorted_ids, e, mb, tn * (C::BN / 16), tn * C::COLS, k, n_pairs, K, N_out, out,
                           smem, tid, lane, wave);
@@ -590,7 +594,7 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_wide_kernel(
             const int64_t logical = t_begin + n_full + wg / QS;
             const int sub = wg % QS;
             const int tn = (int)(logical % n_tiles), mb = (int)(logical / n_tiles);
-            const int e = block_expert[mb];
+            const int e = block_expert[mb / AM];
             if (e >= 0)
                 wide_tile<CQ, Y16>(a_src, w, sorted_ids, e, mb, tn * (C::BN / 16) + sub * (CQ::BN / 16),
                                    tn * C::COLS + sub * CQ::COLS, k, n_pairs, K, N_out, out, smem, tid, lane, wave);
@@ -598,7 +602,7 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_wide_kernel(
     }
 }
 
-template <class C, bool Y16>
+template <class C, bool Y16, int AM = 1>
 static int launch_wide(const void* a, const void* w, const int32_t* sorted_ids, const int32_t* block_expert,
                        const int32_t* num_padded, int k, int64_t n_pairs, int K, int N_out, int64_t cap, void* out,
                        hipStream_t s, const char* what) {
@@ -625,9 +629,9 @@ static int launch_wide(const void* a, const void* w, const int32_t* sorted_ids, 
     constexpr bool SPLIT = !C::GATED;  // quarter tiles for the down projection's last round
     static std::atomic<uint64_t> lds_set{0};
     const int rc =
-        ensure_dynamic_lds((const void*)grouped_gemm_wide_kernel<C, Y16, SPLIT>, (int)lds, lds_set, what);
+        ensure_dynamic_lds((const void*)grouped_gemm_wide_kernel<C, Y16, SPLIT, AM>, (int)lds, lds_set, what);
     if (rc) return rc;
-    hipLaunchKernelGGL((grouped_gemm_wide_kernel<C, Y16, SPLIT>), dim3((unsigned)grid), dim3(C::THREADS), lds, s,
+    hipLaunchKernelGGL((grouped_gemm_wide_kernel<C, Y16, SPLIT, AM>), dim3((unsigned)grid), dim3(C::THREADS), lds, s,
                        (const uint16_t*)a, (const uint16_t*)w, sorted_ids, block_expert, num_padded, k, n_pairs, K,
                        N_out, n_tiles, out);
     return check_launch(what);
@@ -825,8 +829,11 @@ static int dispatch_gemm(int32_t block_m, const void* a, const void* w, const in
         case 128:
             return launch_wide<WideCfg<GATED, 128, GATED ? 4 : 3>, Y16>(a, w, sorted_ids, block_expert, num_padded, k, n_pairs, K,
                                                        N_out, cap, out, s, what);
+        case 256:  // two 128-row tiles per grouping block: the same bits as block_m 128 for every row
+            return launch_wide<WideCfg<GATED, 128, GATED ? 4 : 3>, Y16, 2>(a, w, sorted_ids, block_expert, num_padded,
+                                                                          k, n_pairs, K, N_out, cap, out, s, what);
     }
-    return set_error(MOE_ERR_UNSUPPORTED, "%s: block_m=%d not in {16,32,64,128}", what, block_m);
+    return set_error(MOE_ERR_UNSUPPORTED, "%s: block_m=%d not in {16,32,64,128,256}", what, block_m);
 }
 
 static int check_gemm_args(const char* fn, const void* a, const void* w, const int32_t* sorted_ids,
@@ -834,7 +841,8 @@ static int check_gemm_args(const char* fn, const void* a, const void* w, const i
                            int32_t I, int32_t E, int32_t block_m, int64_t cap, const void* out) {
     int rc = check_shape(fn, T, H, E, k, I);
     if (rc) return rc;
-    if (!valid_block_m(block_m)) return set_error(MOE_ERR_UNSUPPORTED, "%s: block_m=%d not in {16,32,64,128}", fn, block_m);
+    if (!valid_block_m(block_m))
+        return set_error(MOE_ERR_UNSUPPORTED, "%s: block_m=%d not in {16,32,64,128,256}", fn, block_m);
     if (T == 0) return MOE_OK;
     if (!a || !w || !sorted_ids || !block_expert || !num_padded || !out)
         return set_error(MOE_ERR_INVALID, "%s: required pointer is NULL", fn);

@@ -155,9 +155,12 @@ def test_skinny_kernel_loads_in_bounds(T, H, E, k, I):
     _check(b, E * H * I, "w2")
 
 
-def _wide_copies(gated, bm, sorted_ids, block_expert, npad, T, k, K, N_out, E, bn=512, waves=None):
+def _wide_copies(gated, bm, sorted_ids, block_expert, npad, T, k, K, N_out, E, bn=512, am=1):
     """Byte offsets of the wide kernel's direct-to-LDS copies (activations
-    relative to x or act, weights relative to the whole packed weight)."""
+    relative to x or act, weights relative to the whole packed weight). bm
+    is the tile's rows; with am = 2 the grouping blocks are 2*bm rows (block_m
+    256 computed as two 128-row tiles) and block_expert is indexed per
+    grouping block."""
     lane = np.arange(64)
     w_rows = 2 * N_out if gated else N_out
     bands = w_rows // 16
@@ -166,7 +169,7 @@ def _wide_copies(gated, bm, sorted_ids, block_expert, npad, T, k, K, N_out, E, b
     n_pairs = T * k
     a_offs, b_offs = [], []
     for mb in range(npad // bm):
-        e = int(block_expert[mb])
+        e = int(block_expert[mb // am])
         assert e >= 0
         for tn in range(n_tiles):
             band0 = tn * (bn // 16)
@@ -206,3 +209,15 @@ def test_wide_kernel_copies_in_bounds(bm, T, H, E, k, I):
     # quarter-width down tiles: 128 weight rows from band tn*32 + sub*8
     a, b = _wide_copies(False, bm, sorted_ids, block_expert, npad, T, k, I, H, E, bn=128)
     _check(b, E * H * I, "w2 (quarter tiles)")
+
+
+def test_wide_kernel_copies_in_bounds_block_m_256():
+    T, H, E, k, I = 700, 192, 8, 2, 160
+    sorted_ids, block_expert, npad = _routing(T, k, E, 256, T)
+    cap = len(sorted_ids)
+    a, b = _wide_copies(True, 128, sorted_ids, block_expert, npad, T, k, H, I, E, am=2)
+    _check(a, T * H, "x")
+    _check(b, E * 2 * I * H, "w13")
+    a, b = _wide_copies(False, 128, sorted_ids, block_expert, npad, T, k, I, H, E, am=2)
+    _check(a, cap * I, "act")
+    _check(b, E * H * I, "w2")
