@@ -66,12 +66,18 @@ class OracleLib:
         lib.oracle_fused_add_rmsnorm.restype = None
         lib.oracle_max_threads.argtypes = []
         lib.oracle_max_threads.restype = ci
+        lib.oracle_set_threads.argtypes = [ci]
+        lib.oracle_set_threads.restype = None
         self.path = path
         self._lib = lib
 
     def max_threads(self) -> int:
         """OpenMP threads the oracle's parallel loops use."""
         return int(self._lib.oracle_max_threads())
+
+    def set_threads(self, n: int) -> None:
+        """Threads for the oracle's later parallel loops (for timing runs)."""
+        self._lib.oracle_set_threads(int(n))
 
     def router_logits(self, x: np.ndarray, w_router: np.ndarray, bias: Optional[np.ndarray] = None) -> np.ndarray:
         """fp64 logits [T, E] from bf16 x [T, H] and w_router [E, H] (+ fp32 bias [E])."""

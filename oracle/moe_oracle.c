@@ -61,6 +61,16 @@ int oracle_max_threads(void) {
 #endif
 }
 
+/* Threads the later parallel regions use (n >= 1): a thread-count control
+ * for timing the oracle, no arithmetic. */
+void oracle_set_threads(int n) {
+#ifdef _OPENMP
+    if (n >= 1) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 static double bf16_value(uint16_t bits) {
     uint32_t u = (uint32_t)bits << 16;
     float f;
