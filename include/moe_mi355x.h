@@ -72,6 +72,9 @@ extern "C" {
 #define MOE_OUT_BF16 MOE_DTYPE_BF16
 #define MOE_OUT_FP32 MOE_DTYPE_FP32
 
+/* Size of the static device scratch of moe_align_by_expert_noalloc. */
+#define MOE_ALIGN_NOALLOC_MAX_WORKSPACE_BYTES 262144
+
 /* Version of this ABI (MOE_ABI_VERSION). */
 int moe_abi_version(void);
 
@@ -140,6 +143,25 @@ size_t moe_align_workspace_bytes(int64_t T, int32_t k, int32_t E, int32_t block_
 int moe_align_by_expert(const int32_t* topk_ids, int64_t T, int32_t k, int32_t E, int32_t block_m,
                         int32_t* sorted_ids, int32_t* block_expert, int32_t* expert_counts, int32_t* num_padded,
                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * moe_align_by_expert without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc). Same arguments, results and guarantees as
+ * moe_align_by_expert; the per-tile histograms go to a static device array of
+ * MOE_ALIGN_NOALLOC_MAX_WORKSPACE_BYTES (256 KB) that each GPU the
+ * library runs on holds until the process ends. The call allocates and frees
+ * nothing. Calls whose moe_align_workspace_bytes(T, k, E, block_m) exceeds
+ * MOE_ALIGN_NOALLOC_MAX_WORKSPACE_BYTES (more than 65536 / E tiles: T*k above about 1M pairs at E = 256)
+ * return MOE_ERR_UNSUPPORTED and enqueue nothing. Every call on one GPU uses
+ * the same array: calls that may overlap on one GPU (different streams, or
+ * host threads enqueueing concurrently) race and must be serialised by the
+ * caller. The first call on each device looks up that device's copy of the
+ * array (hipGetSymbolAddress) and may return MOE_ERR_HIP if that fails.
+ */
+int moe_align_by_expert_noalloc(const int32_t* topk_ids, int64_t T, int32_t k, int32_t E, int32_t block_m,
+                                int32_t* sorted_ids, int32_t* block_expert, int32_t* expert_counts,
+                                int32_t* num_padded, void* stream);
 
 /* Bytes of a packed [E, N, K] bf16 weight (equal to the row-major size), or
  * 0 when the shape cannot be packed (needs N % 16 == 0 and K % 32 == 0). */

@@ -21,6 +21,8 @@ from ._lib import (  # noqa: F401
     lib,
     moe_abi_version,
     moe_align_by_expert,
+    moe_align_by_expert_noalloc,
+    moe_align_noalloc_max_workspace_bytes,
     moe_align_capacity,
     moe_align_workspace_bytes,
     moe_combine,

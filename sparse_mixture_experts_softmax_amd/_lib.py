@@ -28,6 +28,7 @@ MOE_DTYPE_FP32 = 1
 MOE_DTYPE_FP16 = 2
 MOE_OUT_BF16 = MOE_DTYPE_BF16
 MOE_OUT_FP32 = MOE_DTYPE_FP32
+MOE_ALIGN_NOALLOC_MAX_WORKSPACE_BYTES = 262144
 _Y_DTYPES = {torch.float16: MOE_DTYPE_FP16, torch.float32: MOE_DTYPE_FP32}
 
 EXPORTS = (
@@ -37,6 +38,7 @@ EXPORTS = (
     "moe_align_capacity",
     "moe_align_workspace_bytes",
     "moe_align_by_expert",
+    "moe_align_by_expert_noalloc",
     "moe_grouped_gemm_gate_up_silu",
     "moe_grouped_gemm_down",
     "moe_combine",
@@ -74,6 +76,8 @@ def lib():
         L.moe_align_capacity.argtypes, L.moe_align_capacity.restype = [i64, i32, i32, i32], i64
         L.moe_align_workspace_bytes.argtypes, L.moe_align_workspace_bytes.restype = [i64, i32, i32, i32], sz
         L.moe_align_by_expert.argtypes = [p, i64, i32, i32, i32, p, p, p, p, p, sz, p]
+        L.moe_align_by_expert_noalloc.argtypes = [p, i64, i32, i32, i32, p, p, p, p, p]
+        L.moe_align_by_expert_noalloc.restype = ctypes.c_int
         L.moe_grouped_gemm_gate_up_silu.argtypes = [p, p, p, p, p, i64, i32, i32, i32, i32, i32, i64, p, p]
         L.moe_grouped_gemm_down.argtypes = [p, p, p, p, p, i64, i32, i32, i32, i32, i32, i64, p, i32, p]
         L.moe_combine.argtypes = [p, i32, p, i64, i32, i32, p, i32, p]
@@ -268,3 +272,24 @@ def moe_combine(y, topk_weights, T: int, k: int, H: int, out, stream=None):
     p = _ptrs((y, y.dtype, "y", False, T * k * H), (topk_weights, torch.float32, "topk_weights", False, T * k),
               (out, out.dtype, "out", False, T * H))
     _check(lib().moe_combine(p[0], yd, p[1], T, k, H, p[2], od, _stream(stream, y)))
+
+
+def moe_align_noalloc_max_workspace_bytes() -> int:
+    """Static scratch of moe_align_by_expert_noalloc (the header's
+    MOE_ALIGN_NOALLOC_MAX_WORKSPACE_BYTES)."""
+    return MOE_ALIGN_NOALLOC_MAX_WORKSPACE_BYTES
+
+
+def moe_align_by_expert_noalloc(topk_ids, T: int, k: int, E: int, block_m: int, sorted_ids, block_expert,
+                                expert_counts, num_padded, stream=None):
+    """moe_align_by_expert with its histograms in the library's static device
+    scratch (no workspace, nothing allocated); calls on one GPU must not
+    overlap."""
+    i32 = torch.int32
+    _nonneg(T=T, k=k, E=E)
+    cap = max(0, lib().moe_align_capacity(T, k, E, block_m))
+    p = _ptrs((topk_ids, i32, "topk_ids", False, T * k), (sorted_ids, i32, "sorted_ids", False, cap),
+              (block_expert, i32, "block_expert", False, cap // max(block_m, 1)),
+              (expert_counts, i32, "expert_counts", False, E), (num_padded, i32, "num_padded", False, 1))
+    _check(lib().moe_align_by_expert_noalloc(p[0], T, k, E, block_m, p[1], p[2], p[3], p[4],
+                                             _stream(stream, topk_ids)))

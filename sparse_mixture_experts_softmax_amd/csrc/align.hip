@@ -17,6 +17,8 @@
 // sentinel into the pad rows and the block owners of its share of the
 // capacity. When all pairs fit one tile, kernel 2 counts them itself and
 // kernel 1 is skipped.
+#include <mutex>
+
 #include "abi_util.h"
 #include "moe_common.h"
 
@@ -217,6 +219,45 @@ static void launch_align(const int32_t* ids, int64_t n, int E, int BM, int64_t c
                        num_padded);
 }
 
+// Workspace of moe_align_by_expert_noalloc: the per-tile histograms live in
+// this file-scope device array instead of a caller buffer (each device holds
+// its own copy for the life of the process). Host code must not pass the
+// array's name to a kernel (on the host it is only a stand-in symbol): its
+// device address comes from hipGetSymbolAddress, taken once per device.
+constexpr int64_t kAlignScratchInts = MOE_ALIGN_NOALLOC_MAX_WORKSPACE_BYTES / sizeof(int32_t);  // ntiles * E counts
+static __device__ __align__(256) int32_t scratch[kAlignScratchInts];
+
+constexpr int kMaxDevices = 64;
+static std::atomic<int32_t*> g_scratch_ptr[kMaxDevices];
+static std::mutex g_scratch_mu;
+
+// Device address of `scratch` on the current device, looked up once per
+// device; nullptr (with the error set) on failure.
+static int32_t* scratch_on_current_device(const char* fn) {
+    int dev = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess) {
+        set_error(MOE_ERR_HIP, "%s: hipGetDevice: %s", fn, hipGetErrorString(err));
+        return nullptr;
+    }
+    if (dev < 0 || dev >= kMaxDevices) {
+        set_error(MOE_ERR_UNSUPPORTED, "%s: device %d beyond the %d this library tracks", fn, dev, kMaxDevices);
+        return nullptr;
+    }
+    int32_t* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (p) return p;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (p) return p;
+    err = hipGetSymbolAddress((void**)&p, HIP_SYMBOL(scratch));
+    if (err != hipSuccess || p == nullptr) {
+        set_error(MOE_ERR_HIP, "%s: hipGetSymbolAddress(scratch): %s", fn, hipGetErrorString(err));
+        return nullptr;
+    }
+    g_scratch_ptr[dev].store(p, std::memory_order_release);
+    return p;
+}
+
 }  // namespace moe
 
 extern "C" int64_t moe_align_capacity(int64_t T, int32_t k, int32_t E, int32_t block_m) {
@@ -232,31 +273,30 @@ extern "C" size_t moe_align_workspace_bytes(int64_t T, int32_t k, int32_t E, int
     return ntiles <= 1 ? 0 : (size_t)ntiles * (size_t)E * sizeof(int32_t);
 }
 
-extern "C" int moe_align_by_expert(const int32_t* topk_ids, int64_t T, int32_t k, int32_t E, int32_t block_m,
-                                   int32_t* sorted_ids, int32_t* block_expert, int32_t* expert_counts,
-                                   int32_t* num_padded, void* workspace, size_t workspace_bytes, void* stream) {
-    using namespace moe;
-    clear_error();
-    if (T < 0 || k < 0 || E < 0) return set_error(MOE_ERR_INVALID, "moe_align_by_expert: negative size");
-    if (E < 1 || E > kMaxExperts)
-        return set_error(MOE_ERR_UNSUPPORTED, "moe_align_by_expert: E=%d outside [1, 256]", E);
-    if (k < 1 || k > E || k > kMaxTopK) return set_error(MOE_ERR_UNSUPPORTED, "moe_align_by_expert: k=%d invalid", k);
+namespace moe {
+
+// Checks shared by both align entry points; MOE_OK with T > 0 means launch.
+static int check_align_args(const char* fn, const int32_t* topk_ids, int64_t T, int32_t k, int32_t E,
+                            int32_t block_m, const int32_t* sorted_ids, const int32_t* block_expert,
+                            const int32_t* expert_counts, const int32_t* num_padded) {
+    if (T < 0 || k < 0 || E < 0) return set_error(MOE_ERR_INVALID, "%s: negative size", fn);
+    if (E < 1 || E > kMaxExperts) return set_error(MOE_ERR_UNSUPPORTED, "%s: E=%d outside [1, 256]", fn, E);
+    if (k < 1 || k > E || k > kMaxTopK) return set_error(MOE_ERR_UNSUPPORTED, "%s: k=%d invalid", fn, k);
     if (!valid_block_m(block_m))
-        return set_error(MOE_ERR_UNSUPPORTED, "moe_align_by_expert: block_m=%d not in {16,32,64,128}", block_m);
-    if (T * (int64_t)k >= ((int64_t)1 << 31))
-        return set_error(MOE_ERR_UNSUPPORTED, "moe_align_by_expert: T*k too large");
+        return set_error(MOE_ERR_UNSUPPORTED, "%s: block_m=%d not in {16,32,64,128}", fn, block_m);
+    if (T * (int64_t)k >= ((int64_t)1 << 31)) return set_error(MOE_ERR_UNSUPPORTED, "%s: T*k too large", fn);
     if (T == 0) return MOE_OK;
     if (!topk_ids || !sorted_ids || !block_expert || !expert_counts || !num_padded)
-        return set_error(MOE_ERR_INVALID, "moe_align_by_expert: required pointer is NULL");
+        return set_error(MOE_ERR_INVALID, "%s: required pointer is NULL", fn);
+    return MOE_OK;
+}
+
+static int run_align(const int32_t* topk_ids, int64_t T, int32_t k, int32_t E, int32_t block_m, int32_t* sorted_ids,
+                     int32_t* block_expert, int32_t* expert_counts, int32_t* num_padded, int32_t* ws,
+                     hipStream_t s, const char* fn) {
     const int64_t ntiles = align_ntiles(T, k);
-    const size_t need = moe_align_workspace_bytes(T, k, E, block_m);
-    if (need > 0 && (workspace == nullptr || workspace_bytes < need))
-        return set_error(MOE_ERR_WORKSPACE, "moe_align_by_expert: workspace of %zu bytes needed, %zu given", need,
-                         workspace_bytes);
     const int64_t cap = moe_align_capacity(T, k, E, block_m);
     const int64_t n = T * k;
-    hipStream_t s = (hipStream_t)stream;
-    int32_t* ws = (int32_t*)workspace;
     switch (align_per_thread(T, k)) {
         case 4:
             launch_align<4>(topk_ids, n, E, block_m, cap, ntiles, ws, sorted_ids, block_expert, expert_counts,
@@ -270,5 +310,50 @@ extern "C" int moe_align_by_expert(const int32_t* topk_ids, int64_t T, int32_t k
             launch_align<16>(topk_ids, n, E, block_m, cap, ntiles, ws, sorted_ids, block_expert, expert_counts,
                              num_padded, s);
     }
-    return check_launch("moe_align_by_expert");
+    return check_launch(fn);
 }
+
+}  // namespace moe
+
+extern "C" int moe_align_by_expert(const int32_t* topk_ids, int64_t T, int32_t k, int32_t E, int32_t block_m,
+                                   int32_t* sorted_ids, int32_t* block_expert, int32_t* expert_counts,
+                                   int32_t* num_padded, void* workspace, size_t workspace_bytes, void* stream) {
+    using namespace moe;
+    clear_error();
+    const char* fn = "moe_align_by_expert";
+    int rc = check_align_args(fn, topk_ids, T, k, E, block_m, sorted_ids, block_expert, expert_counts, num_padded);
+    if (rc || T == 0) return rc;
+    const size_t need = moe_align_workspace_bytes(T, k, E, block_m);
+    if (need > 0 && (workspace == nullptr || workspace_bytes < need))
+        return set_error(MOE_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
+                         workspace_bytes);
+    return run_align(topk_ids, T, k, E, block_m, sorted_ids, block_expert, expert_counts, num_padded,
+                     (int32_t*)workspace, (hipStream_t)stream, fn);
+}
+
+extern "C" int moe_align_by_expert_noalloc(const int32_t* topk_ids, int64_t T, int32_t k, int32_t E,
+                                           int32_t block_m, int32_t* sorted_ids, int32_t* block_expert,
+                                           int32_t* expert_counts, int32_t* num_padded, void* stream) {
+    using namespace moe;
+    clear_error();
+    const char* fn = "moe_align_by_expert_noalloc";
+    int rc = check_align_args(fn, topk_ids, T, k, E, block_m, sorted_ids, block_expert, expert_counts, num_padded);
+    if (rc || T == 0) return rc;
+    const size_t need = moe_align_workspace_bytes(T, k, E, block_m);
+    if (need > (size_t)MOE_ALIGN_NOALLOC_MAX_WORKSPACE_BYTES)
+        return set_error(MOE_ERR_UNSUPPORTED,
+                         "%s: T*k=%lld pairs over E=%d experts need %zu bytes of per-tile histograms, beyond the "
+                         "%d-byte static scratch; use moe_align_by_expert with a workspace",
+                         fn, (long long)(T * k), E, need, MOE_ALIGN_NOALLOC_MAX_WORKSPACE_BYTES);
+    int32_t* ws = nullptr;
+    if (need > 0) {
+        // every entry the scatter kernel reads is first written by the
+        // histogram kernel of the same call, so the scratch needs no clearing
+        ws = scratch_on_current_device(fn);
+        if (!ws) return MOE_ERR_HIP;
+    }
+    return run_align(topk_ids, T, k, E, block_m, sorted_ids, block_expert, expert_counts, num_padded, ws,
+                     (hipStream_t)stream, fn);
+}
+
+

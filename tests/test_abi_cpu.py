@@ -275,3 +275,21 @@ def test_layer_rejects_buffers_of_another_shape():
 def test_binding_rejects_negative_sizes():
     with pytest.raises(ValueError, match="non-negative"):
         moe.moe_combine(_t(8, torch.float16), _t(1, torch.float32), -1, 1, 64, _t(64, torch.bfloat16))
+
+
+def test_noalloc_align_validation_without_gpu():
+    """The allocation-free grouping call checks its arguments on the host:
+    invalid shapes and sizes beyond its static scratch are refused before any
+    device work, and T = 0 succeeds."""
+    L = _raw()
+    args = (FAKE, FAKE, FAKE, FAKE, NULL)
+    assert L.moe_align_by_expert_noalloc(FAKE, 16, 2, 8, 48, *args) == _lib.MOE_ERR_UNSUPPORTED
+    assert L.moe_align_by_expert_noalloc(FAKE, -1, 2, 8, 16, *args) == _lib.MOE_ERR_INVALID
+    assert L.moe_align_by_expert_noalloc(FAKE, 0, 2, 8, 16, *args) == _lib.MOE_OK
+    assert L.moe_align_by_expert_noalloc(NULL, 16, 2, 8, 16, *args) == _lib.MOE_ERR_INVALID
+    T, k, E, bm = 300000, 8, 256, 128
+    assert moe.moe_align_workspace_bytes(T, k, E, bm) > moe.moe_align_noalloc_max_workspace_bytes()
+    assert L.moe_align_by_expert_noalloc(FAKE, T, k, E, bm, *args) == _lib.MOE_ERR_UNSUPPORTED
+    assert "static scratch" in moe.moe_last_error()
+    hdr = open(HEADER).read()
+    assert f"#define MOE_ALIGN_NOALLOC_MAX_WORKSPACE_BYTES {moe.moe_align_noalloc_max_workspace_bytes()}" in hdr
