@@ -136,11 +136,13 @@ def kernel_label(kind: str, block_m: int) -> str:
     row-block size (as rocprofv3 lists it, template arguments shortened)."""
     if kind == "gate_up":
         return {16: "grouped_gemm_skinny_kernel<true,1,2,8,false>", 32: "grouped_gemm_kernel<GemmCfg<32,128,true>,false>",
-                64: "grouped_gemm_wide_kernel<WideCfg<true,64,4,4,2,128>,false,false>",
-                128: "grouped_gemm_wide_kernel<WideCfg<true,128,4,4,2,128>,false,false>"}[block_m]
+                64: "grouped_gemm_wide_kernel<WideCfg<true,64,4,4,2,128>,false,false,1>",
+                128: "grouped_gemm_wide_kernel<WideCfg<true,128,4,4,2,128>,false,false,1>",
+                256: "grouped_gemm_wide_kernel<WideCfg<true,128,4,4,2,128>,false,false,2>"}[block_m]
     return {16: "grouped_gemm_skinny_kernel<false,4,4,4,true>", 32: "grouped_gemm_kernel<GemmCfg<32,128,false>,true>",
-            64: "grouped_gemm_wide_kernel<WideCfg<false,64,4,4,2,128>,true,true>",
-            128: "grouped_gemm_wide_kernel<WideCfg<false,128,3,4,2,128>,true,true>"}[block_m]
+            64: "grouped_gemm_wide_kernel<WideCfg<false,64,4,4,2,128>,true,true,1>",
+            128: "grouped_gemm_wide_kernel<WideCfg<false,128,3,4,2,128>,true,true,1>",
+            256: "grouped_gemm_wide_kernel<WideCfg<false,128,3,4,2,128>,true,true,2>"}[block_m]
 
 
 def host_cpu_model() -> str:
@@ -521,6 +523,35 @@ def _stats(directory: str, prefix: str):
     return out
 
 
+def stats_command(workload: str) -> str:
+    return (f"rocprofv3 --kernel-trace --stats --output-format csv -d DIR -o {workload} -- python3 -u bench.py "
+            f"--workload {workload} --also none --steps 50 --warmup 20 --cpu-seconds 0")
+
+
+def record_stats(directory: str, workload: str):
+    """profiles/<workload>_kernel_stats.md from the kernel-trace run of
+    ``stats_command(workload)``."""
+    import synth
+
+    files = glob.glob(os.path.join(directory, "**", f"{workload}_kernel_stats.csv"), recursive=True)
+    if not files:
+        return
+    shape = synth.CONFIGS[workload]
+    lines = [f"# rocprofv3 kernel statistics: {WORKLOAD_TEXT[workload]} (T={shape.T}, H={shape.H}, E={shape.E}, "
+             f"k={shape.k}, I={shape.I})", "",
+             "Whole bench run (20 warm-up and 3 x 50 timed steps, plus the one-time weight packing and copies), "
+             "from the repository root on one MI355X (`export TMPDIR=/tmp` first; DIR = the output directory):", "",
+             "```", stats_command(workload), "```", "",
+             "| kernel | calls | average (us) | min (us) | max (us) | share of GPU time |", "|---|---|---|---|---|---|"]
+    with open(files[0]) as fh:
+        for r in csv.DictReader(fh):
+            lines.append(f"| `{r['Name'].split('(')[0]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                         f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                         f"{float(r['Percentage']):.1f}% |")
+    with open(os.path.join(ROOT, "profiles", f"{workload}_kernel_stats.md"), "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+
+
 def record_counters(directory: str, workload: str):
     """Parse the counter passes of ``counter_commands(workload)`` from
     ``directory`` into profiles/counters.json and a summary table."""
@@ -615,6 +646,7 @@ def main():
     args = ap.parse_args()
 
     if args.record_counters:
+        record_stats(args.record_counters, args.workload)
         record_counters(args.record_counters, args.workload)
         return
     if args.gpus != 1:
