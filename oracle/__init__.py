@@ -36,7 +36,8 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "moe_oracle.c")
-_LIB_PATH = os.path.join(_HERE, "libmoe_oracle.so")
+# MOE_ORACLE_LIB names another build (the host-sanitizer test build).
+_LIB_PATH = os.environ.get("MOE_ORACLE_LIB") or os.path.join(_HERE, "libmoe_oracle.so")
 
 
 class OracleLib:

@@ -16,7 +16,9 @@ from typing import Optional
 import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libmoe_mi355x.so")
+# MOE_MI355X_LIB names another build of the library (e.g. the host-sanitizer
+# test build); there is still no fallback when it is missing.
+LIB_PATH = os.environ.get("MOE_MI355X_LIB") or os.path.join(HERE, "libmoe_mi355x.so")
 
 MOE_OK = 0
 MOE_ERR_INVALID = -1

@@ -60,10 +60,17 @@ def _scratch_users(remarks: str) -> list:
     return bad
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
+# Host-side AddressSanitizer + UndefinedBehaviorSanitizer (argument checks,
+# launch set-up, error paths): each flag applies to the host compilation only,
+# the device code is built as usual.
+HOST_SANITIZE = ["-Xarch_host", "-fsanitize=address,undefined", "-Xarch_host", "-fno-sanitize-recover=undefined",
+                 "-Xarch_host", "-fno-omit-frame-pointer", "-g"]
+
+
+def _compile(src: str, build_dir: str = BUILD_DIR, extra=()) -> str:
+    obj = os.path.join(build_dir, os.path.basename(src) + ".o")
     remarks = ["-Rpass-analysis=kernel-resource-usage"] if src.endswith(".hip") else []
-    cmd = [hipcc(), *HIP_FLAGS, *remarks, f"-I{INCLUDE}", f"-I{CSRC}", "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *HIP_FLAGS, *extra, *remarks, f"-I{INCLUDE}", f"-I{CSRC}", "-c", os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{res.stdout}\n{res.stderr}")
@@ -73,19 +80,24 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(jobs: int = 0) -> str:
-    """Compile all sources and link the shared library; returns its path."""
-    os.makedirs(BUILD_DIR, exist_ok=True)
+def build(jobs: int = 0, out: str = LIB_PATH, host_sanitize: bool = False) -> str:
+    """Compile all sources and link the shared library; returns its path.
+    ``host_sanitize``: instrument the host code with ASan and UBSan (a test
+    build, loaded with the sanitizer runtime preloaded; written to ``out``)."""
+    build_dir = BUILD_DIR if not host_sanitize else os.path.join(os.path.dirname(os.path.abspath(out)), "_objs")
+    os.makedirs(build_dir, exist_ok=True)
+    extra = HOST_SANITIZE if host_sanitize else []
     jobs = jobs or min(len(SOURCES), os.cpu_count() or 1, 16)
     with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB_PATH + ".tmp"
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+        objs = list(ex.map(lambda src: _compile(src, build_dir, extra), SOURCES))
+    tmp = out + ".tmp"
+    link_extra = ["-Xarch_host", "-fsanitize=address,undefined", "-shared-libasan"] if host_sanitize else []
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *link_extra, *objs, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{res.stdout}\n{res.stderr}")
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

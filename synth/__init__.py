@@ -29,7 +29,8 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "synth.c")
-_LIB_PATH = os.path.join(_HERE, "libmoe_synth.so")
+# MOE_SYNTH_LIB names another build (the host-sanitizer test build).
+_LIB_PATH = os.environ.get("MOE_SYNTH_LIB") or os.path.join(_HERE, "libmoe_synth.so")
 _lib = None
 
 MARGIN = 1e-3  # minimum adjacent gap among each token's k+1 largest fp64 logits
