@@ -43,9 +43,12 @@
  *    returns a thread-local message describing the last failure.
  *  - Limits: 1 <= E <= 256, 1 <= k <= min(E, 32), H % 64 == 0, I % 32 == 0,
  *    T >= 0 (T == 0 is a successful no-op), T * k < 2^31,
- *    block_m in {16, 32, 64, 128}; with block_m 64 or 128 the grouped GEMMs'
- *    activation operand (x: T*H*2 bytes; act: cap*I*2 bytes) and one expert's
- *    weights must each be under 4 GiB (the copies use 32-bit offsets).
+ *    block_m in {16, 32, 64, 128, 256} (256: the grouping pads each expert to
+ *    256 rows and the GEMMs compute each such block as two 128-row tiles, so
+ *    every output equals block_m 128's bit for bit); with block_m 64 or more
+ *    the grouped GEMMs' activation operand (x: T*H*2 bytes; act: cap*I*2
+ *    bytes) and one expert's weights must each be under 4 GiB (the copies use
+ *    32-bit offsets).
  */
 #ifndef MOE_MI355X_H
 #define MOE_MI355X_H

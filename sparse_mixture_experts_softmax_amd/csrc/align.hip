@@ -283,7 +283,7 @@ static int check_align_args(const char* fn, const int32_t* topk_ids, int64_t T, 
     if (E < 1 || E > kMaxExperts) return set_error(MOE_ERR_UNSUPPORTED, "%s: E=%d outside [1, 256]", fn, E);
     if (k < 1 || k > E || k > kMaxTopK) return set_error(MOE_ERR_UNSUPPORTED, "%s: k=%d invalid", fn, k);
     if (!valid_block_m(block_m))
-        return set_error(MOE_ERR_UNSUPPORTED, "%s: block_m=%d not in {16,32,64,128}", fn, block_m);
+        return set_error(MOE_ERR_UNSUPPORTED, "%s: block_m=%d not in {16,32,64,128,256}", fn, block_m);
     if (T * (int64_t)k >= ((int64_t)1 << 31)) return set_error(MOE_ERR_UNSUPPORTED, "%s: T*k too large", fn);
     if (T == 0) return MOE_OK;
     if (!topk_ids || !sorted_ids || !block_expert || !expert_counts || !num_padded)

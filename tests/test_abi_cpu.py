@@ -37,6 +37,8 @@ def test_capacity_and_workspace():
     assert moe.moe_align_capacity(1, 1, 256, 128) == 128
     assert moe.moe_align_capacity(0, 8, 128, 64) == 0
     assert moe.moe_align_capacity(10, 2, 8, 48) == -1
+    assert moe.moe_align_capacity(10, 2, 8, 512) == -1
+    assert moe.moe_align_capacity(64, 8, 128, 256) == (512 + 128 * 255 + 255) // 256 * 256
     assert moe.moe_align_workspace_bytes(64, 8, 128, 16) == 0  # one tile: no workspace
     assert moe.moe_align_workspace_bytes(16384, 8, 128, 64) == 32 * 128 * 4  # 32 tiles of 4096 pairs
     assert moe.moe_align_workspace_bytes(4096, 8, 128, 64) == 32 * 128 * 4  # 32 tiles of 1024 pairs
