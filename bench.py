@@ -322,6 +322,29 @@ def measure_layer(workload: str, steps: int, warmup: int, seed: int, weights: We
     gu_ms = float(np.mean([m[gu][0].elapsed_time(m[gu][1]) for m in marks]))
     dn_ms = float(np.mean([m[dn][0].elapsed_time(m[dn][1]) for m in marks]))
 
+    # A/B: the down projection and the combine as one launch
+    # (moe_grouped_gemm_down_combine), same buffers, same number of steps
+    fused_ms = None
+    if not dense:
+        fused_call = lambda w13, w2: moe.moe_grouped_gemm_down_combine(  # noqa: E731
+            b.act, w2, b.sorted_ids, b.block_expert, b.num_padded, b.topk_weights, T, k, H, I, E, block_m, b.cap, b.y,
+            b.counters, b.out, sp)
+
+        def fused_step(c):
+            w13, w2 = w13s[c % copies], w2s[c % copies]
+            for call in calls[:3]:
+                call(w13, w2)
+            fused_call(w13, w2)
+
+        for i in range(warmup):
+            fused_step(i)
+        torch.cuda.synchronize()
+        t2 = time.perf_counter()
+        for i in range(steps):
+            fused_step(i)
+        torch.cuda.synchronize()
+        fused_ms = (time.perf_counter() - t2) * 1e3 / steps
+
     n_break = min(steps, 50)
     all_marks = [{j: new_events() for j in range(len(calls))} for _ in range(n_break)]
     for i in range(n_break):
@@ -379,6 +402,10 @@ def measure_layer(workload: str, steps: int, warmup: int, seed: int, weights: We
         },
         "roofline": roofline("gate_up", gu_ms),
         "down_roofline": roofline("down", dn_ms),
+        "fused_combine": None if fused_ms is None else {
+            "ms_per_step": round(fused_ms, 5), "tokens_per_s": round(T / (fused_ms * 1e-3), 1),
+            "note": "down projection and weighted combine as one launch (moe_grouped_gemm_down_combine), "
+                    f"{steps} steps timed like ms_per_step"},
     }
     del packed, w13s, w2s, b, x, wr
     torch.cuda.synchronize()
@@ -439,6 +466,7 @@ def norm_bench(args):
                      "frac": round(achieved / PEAK_HBM_GBPS, 4), "kernel": "fused_add_rmsnorm_kernel<1>",
                      "kernel_ms": round(kern_ms, 5), "algorithmic_per_launch": nbytes, "traffic": None},
     }
+    result["norm_route_ab"] = norm_route_ab(args)
     if args.cpu_seconds > 0:
         import oracle
 
@@ -456,6 +484,59 @@ def norm_bench(args):
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)
+
+
+def norm_route_ab(args):
+    """The residual add + RMSNorm before the router, as the standalone kernel
+    followed by moe_route, against moe_fused_add_rmsnorm_route (the norm
+    inside the router's read of x), at the decode and prefill shapes
+    (E = 128, k = 8): mean microseconds per pair of calls / per fused call,
+    HIP events around each of K repetitions."""
+    import numpy as np
+    import torch
+
+    import synth
+    import sparse_mixture_experts_softmax_amd as moe
+
+    out = {}
+    for name, T in (("decode", 64), ("prefill", 4096)):
+        H, E, k = 2048, 128, 8
+        dev = lambda a: torch.from_numpy(a).view(torch.bfloat16).cuda()  # noqa: E731
+        x = dev(synth.normal_bf16(args.seed, synth.TAG_X, (T, H), 1.0))
+        r = dev(synth.normal_bf16(args.seed, 0x200, (T, H), 1.0))
+        w = dev(synth.normal_bf16(args.seed, 0x201, (H,), 1.0))
+        wr = dev(synth.normal_bf16(args.seed, synth.TAG_WR, (E, H), 0.02))
+        xs, rs = x.clone(), r.clone()
+        xo, ro = torch.empty_like(x), torch.empty_like(x)
+        lg = torch.empty((T, E), dtype=torch.float32, device="cuda")
+        ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+        wt = torch.empty((T, k), dtype=torch.float32, device="cuda")
+        stream = torch.cuda.current_stream()
+        sp = stream.cuda_stream
+
+        def separate():
+            moe.moe_fused_add_rmsnorm(xs, rs, w, T, H, 1e-6, True, sp)
+            moe.moe_route(xs, wr, None, lg, ids, wt, T, H, E, k, True, sp)
+
+        def fused():
+            moe.moe_fused_add_rmsnorm_route(x, r, w, 1e-6, True, xo, ro, wr, None, lg, ids, wt, T, H, E, k, True, sp)
+
+        res = {}
+        for label, fn in (("separate_us", separate), ("fused_us", fused)):
+            for _ in range(args.warmup + 10):
+                fn()
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(args.steps)]
+            for a, b in evs:
+                a.record(stream)
+                fn()
+                b.record(stream)
+            torch.cuda.synchronize()
+            res[label] = round(float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e3, 2)
+        res["T"] = T
+        out[name] = res
+        progress(f"norm + route {name}: separate {res['separate_us']} us, fused {res['fused_us']} us")
+    return out
 
 
 def copy_calibration(mb: int):
@@ -700,6 +781,7 @@ def main():
         "step_ms_events": head["step_ms_events"],
         "layer": head["layer"],
         "down_roofline": head["down_roofline"],
+        "fused_combine": head["fused_combine"],
         "workloads": extra,
     }
     if args.cpu_seconds > 0:

@@ -243,6 +243,39 @@ int moe_grouped_gemm_down(const void* act, const void* w2, const int32_t* sorted
                           int32_t block_m, int64_t cap, void* y, int32_t y_dtype, void* stream);
 
 /*
+ * moe_grouped_gemm_down and moe_combine in one launch ([MoE]: the expert
+ * outputs weighted by their scores and summed, at the end of the layer):
+ * the down projection stores each expert output row in y as
+ * moe_grouped_gemm_down does, and the weighted sum of a token's k rows is
+ * formed, inside the same kernel, by the workgroup that completes the
+ * token's last slot for a group of 128 output columns (a device-scope
+ * arrival count per (token, group) with release/acquire ordering). out is
+ * computed exactly as moe_combine computes it (fp32, slots in order), so it
+ * does not depend on which workgroup sums a group: every output is
+ * bit-for-bit reproducible.
+ *
+ *   topk_weights  [T, k] fp32, device (as for moe_combine).
+ *   y             [T*k, H], device, y_dtype (fp16 or fp32), written as by
+ *                 moe_grouped_gemm_down and read back by the kernel.
+ *   counters      [moe_combine_counter_count(T, H)] int32, device: must be all
+ *                 zero on entry; every call that returns MOE_OK leaves them
+ *                 zero (zero them once when allocating).
+ *   out           [T, H], device: bf16 (out_dtype MOE_OUT_BF16, round to
+ *                 nearest even) or fp32 (MOE_OUT_FP32).
+ *   (the rest)    as moe_grouped_gemm_down.
+ * Two calls sharing counters must not overlap in time.
+ */
+int moe_grouped_gemm_down_combine(const void* act, const void* w2, const int32_t* sorted_ids,
+                                  const int32_t* block_expert, const int32_t* num_padded, const float* topk_weights,
+                                  int64_t T, int32_t k, int32_t H, int32_t I, int32_t E, int32_t block_m, int64_t cap,
+                                  void* y, int32_t y_dtype, int32_t* counters, void* out, int32_t out_dtype,
+                                  void* stream);
+
+/* Number of int32 counters moe_grouped_gemm_down_combine needs: T times the
+ * number of 128-column groups of H. -1 on invalid arguments. */
+int64_t moe_combine_counter_count(int64_t T, int32_t H);
+
+/*
  * Weighted sum of the k expert outputs of each token ([MoE]: expert outputs
  * weighted by their scores and summed):
  *   out[t, h] = sum_j topk_weights[t, j] * y[t*k + j, h]   (fp32 accumulation,
@@ -277,6 +310,38 @@ int moe_combine(const void* y, int32_t y_dtype, const float* topk_weights, int64
  */
 int moe_fused_add_rmsnorm(void* x, void* residual, const void* weight, int64_t T, int32_t H, float eps,
                           int32_t has_residual, void* stream);
+
+/*
+ * The residual add + RMSNorm that precedes the layer fused into the router's
+ * read of x (handbook page "The op layer: BaseOP and the layers", sections
+ * "Ops: reference implementations and dispatch" and "RMSNorm and the
+ * residual"), then moe_route on the normalized rows. Equivalent to
+ * moe_fused_add_rmsnorm on copies of x and residual followed by moe_route:
+ *   residual_out = bf16(residual + x)   (fp32 add; = x when has_residual == 0)
+ *   x_out = bf16(norm_weight * bf16(residual_out / sqrt(mean(residual_out^2) + eps)))
+ *   logits, topk_ids, topk_weights as moe_route(x_out, w_router, ...)
+ * The router reads x and the residual once per row and writes x_out and
+ * residual_out once, instead of a separate normalization pass over [T, H].
+ * The mean and square root are taken in fp32 with the same summation order
+ * for every batch size, so a row's outputs do not depend on T.
+ *
+ *   x             [T, H] bf16, device, input.
+ *   residual      [T, H] bf16, device, input (ignored, may be NULL, when
+ *                 has_residual == 0: the first layer).
+ *   norm_weight   [H] bf16, device.
+ *   x_out         [T, H] bf16, device, output: the layer's input.
+ *   residual_out  [T, H] bf16, device, output: the new residual stream.
+ *   (the rest)    as moe_route; x_out is what the grouped gate/up GEMM then
+ *                 reads.
+ * Every router workgroup of a block of tokens reads that block's rows, so the
+ * outputs cannot be written in place: x_out and residual_out must not overlap
+ * each other, x or residual (MOE_ERR_INVALID). Limits: those of moe_route and
+ * H <= 16384; eps >= 0.
+ */
+int moe_fused_add_rmsnorm_route(const void* x, const void* residual, const void* norm_weight, float eps,
+                                int32_t has_residual, void* x_out, void* residual_out, const void* w_router,
+                                const float* router_bias, float* logits, int32_t* topk_ids, float* topk_weights,
+                                int64_t T, int32_t H, int32_t E, int32_t k, int32_t norm_topk_prob, void* stream);
 
 /* The block_m the library's GEMMs run fastest with for this routing shape.
  * A tile-size choice only: for a fixed block_m every result is bit-for-bit

@@ -26,8 +26,11 @@ from ._lib import (  # noqa: F401
     moe_align_capacity,
     moe_align_workspace_bytes,
     moe_combine,
+    moe_combine_counter_count,
     moe_fused_add_rmsnorm,
+    moe_fused_add_rmsnorm_route,
     moe_grouped_gemm_down,
+    moe_grouped_gemm_down_combine,
     moe_grouped_gemm_gate_up_silu,
     moe_last_error,
     moe_pack_weights,
@@ -35,4 +38,14 @@ from ._lib import (  # noqa: F401
     moe_pick_block_m,
     moe_route,
 )
-from .layer import MoEBuffers, MoEConfig, PackedExperts, allocate, gated_mlp, moe_layer, pack_experts  # noqa: F401
+from .layer import (  # noqa: F401
+    MoEBuffers,
+    MoEConfig,
+    PackedExperts,
+    allocate,
+    check_buffers,
+    gated_mlp,
+    moe_layer,
+    moe_layer_with_norm,
+    pack_experts,
+)

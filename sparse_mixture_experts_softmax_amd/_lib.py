@@ -44,10 +44,13 @@ EXPORTS = (
     "moe_grouped_gemm_gate_up_silu",
     "moe_grouped_gemm_down",
     "moe_combine",
+    "moe_grouped_gemm_down_combine",
+    "moe_combine_counter_count",
     "moe_pick_block_m",
     "moe_packed_weight_bytes",
     "moe_pack_weights",
     "moe_fused_add_rmsnorm",
+    "moe_fused_add_rmsnorm_route",
 )
 
 
@@ -83,11 +86,18 @@ def lib():
         L.moe_grouped_gemm_gate_up_silu.argtypes = [p, p, p, p, p, i64, i32, i32, i32, i32, i32, i64, p, p]
         L.moe_grouped_gemm_down.argtypes = [p, p, p, p, p, i64, i32, i32, i32, i32, i32, i64, p, i32, p]
         L.moe_combine.argtypes = [p, i32, p, i64, i32, i32, p, i32, p]
+        L.moe_grouped_gemm_down_combine.argtypes = [p, p, p, p, p, p, i64, i32, i32, i32, i32, i32, i64, p, i32, p, p,
+                                                     i32, p]
+        L.moe_grouped_gemm_down_combine.restype = ctypes.c_int
+        L.moe_combine_counter_count.argtypes, L.moe_combine_counter_count.restype = [i64, i32], i64
         L.moe_pick_block_m.argtypes, L.moe_pick_block_m.restype = [i64, i32, i32], i32
         L.moe_packed_weight_bytes.argtypes, L.moe_packed_weight_bytes.restype = [i32, i32, i32], sz
         L.moe_pack_weights.argtypes, L.moe_pack_weights.restype = [p, p, i32, i32, i32, i32, p], ctypes.c_int
         L.moe_fused_add_rmsnorm.argtypes = [p, p, p, i64, i32, ctypes.c_float, i32, p]
         L.moe_fused_add_rmsnorm.restype = ctypes.c_int
+        L.moe_fused_add_rmsnorm_route.argtypes = [p, p, p, ctypes.c_float, i32, p, p, p, p, p, p, p, i64, i32, i32,
+                                                  i32, i32, p]
+        L.moe_fused_add_rmsnorm_route.restype = ctypes.c_int
         for name in ("moe_route", "moe_align_by_expert", "moe_grouped_gemm_gate_up_silu", "moe_grouped_gemm_down",
                      "moe_combine"):
             getattr(L, name).restype = ctypes.c_int
@@ -213,6 +223,24 @@ def moe_fused_add_rmsnorm(x, residual, weight, T: int, H: int, eps: float, has_r
     _check(lib().moe_fused_add_rmsnorm(px, pr, pw, T, H, float(eps), int(bool(has_residual)), _stream(stream, x)))
 
 
+def moe_fused_add_rmsnorm_route(x, residual, norm_weight, eps: float, has_residual: bool, x_out, residual_out,
+                                w_router, router_bias, logits, topk_ids, topk_weights, T: int, H: int, E: int, k: int,
+                                norm_topk_prob: bool, stream=None):
+    """residual_out <- residual + x (or x), x_out <- rmsnorm(residual_out),
+    then the router on x_out, in one pass over the rows (outputs may not
+    overlap the inputs)."""
+    bf, f32, i32 = torch.bfloat16, torch.float32, torch.int32
+    _nonneg(T=T, H=H, E=E, k=k)
+    p = _ptrs((x, bf, "x", False, T * H), (residual, bf, "residual", not has_residual, T * H),
+              (norm_weight, bf, "norm_weight", False, H), (x_out, bf, "x_out", False, T * H),
+              (residual_out, bf, "residual_out", False, T * H), (w_router, bf, "w_router", False, E * H),
+              (router_bias, f32, "router_bias", True, E), (logits, f32, "logits", False, T * E),
+              (topk_ids, i32, "topk_ids", False, T * k), (topk_weights, f32, "topk_weights", False, T * k))
+    _check(lib().moe_fused_add_rmsnorm_route(p[0], p[1] if has_residual else None, p[2], float(eps),
+                                             int(bool(has_residual)), p[3], p[4], p[5], p[6], p[7], p[8], p[9], T, H,
+                                             E, k, int(bool(norm_topk_prob)), _stream(stream, x)))
+
+
 def moe_align_by_expert(topk_ids, T: int, k: int, E: int, block_m: int, sorted_ids, block_expert, expert_counts,
                         num_padded, workspace=None, stream=None):
     i32 = torch.int32
@@ -295,3 +323,30 @@ def moe_align_by_expert_noalloc(topk_ids, T: int, k: int, E: int, block_m: int, 
               (expert_counts, i32, "expert_counts", False, E), (num_padded, i32, "num_padded", False, 1))
     _check(lib().moe_align_by_expert_noalloc(p[0], T, k, E, block_m, p[1], p[2], p[3], p[4],
                                              _stream(stream, topk_ids)))
+
+
+def moe_combine_counter_count(T: int, H: int) -> int:
+    return lib().moe_combine_counter_count(T, H)
+
+
+def moe_grouped_gemm_down_combine(act, w2, sorted_ids, block_expert, num_padded, topk_weights, T: int, k: int, H: int,
+                                  I: int, E: int, block_m: int, cap: int, y, counters, out, stream=None):
+    """Down projection with the weighted combine fused in. ``y`` (fp16 or
+    fp32) holds the expert outputs; ``counters`` (int32, zero, of
+    moe_combine_counter_count(T, H) elements) are left zero; ``out`` dtype
+    (bf16 or fp32) selects the output precision."""
+    if out is None or out.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("out must be a bf16 or fp32 tensor")
+    od = MOE_OUT_FP32 if out.dtype == torch.float32 else MOE_OUT_BF16
+    yd = _y_dtype(y)
+    bf, i32 = torch.bfloat16, torch.int32
+    _nonneg(T=T, k=k, H=H, I=I, E=E, cap=cap)
+    bm = max(block_m, 1)
+    n_cnt = max(0, lib().moe_combine_counter_count(T, H))
+    p = _ptrs((act, bf, "act", False, cap * I), (w2, bf, "w2", False, E * H * I),
+              (sorted_ids, i32, "sorted_ids", False, cap), (block_expert, i32, "block_expert", False, cap // bm),
+              (num_padded, i32, "num_padded", False, 1), (topk_weights, torch.float32, "topk_weights", False, T * k),
+              (y, y.dtype, "y", False, T * k * H), (counters, i32, "counters", False, n_cnt),
+              (out, out.dtype, "out", False, T * H))
+    _check(lib().moe_grouped_gemm_down_combine(p[0], p[1], p[2], p[3], p[4], p[5], T, k, H, I, E, block_m, cap, p[6],
+                                               yd, p[7], p[8], od, _stream(stream, act)))

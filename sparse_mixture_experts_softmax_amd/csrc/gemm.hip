@@ -33,6 +33,104 @@
 
 namespace moe {
 
+// ----------------------------------------------------------------------------
+// Weighted combine fused into the down projection (moe_grouped_gemm_down_combine)
+//
+// A token's k expert outputs come from k different row blocks, computed by
+// different workgroups on different XCDs, so the sum is taken by whichever
+// workgroup finishes a token's last slot: after storing its y rows, a
+// workgroup makes them visible device-wide (release fence: L2 write-back),
+// then counts one arrival per (token, 128-column group) it covered on a
+// device-scope counter; the workgroup whose arrival is the k-th for a
+// (token, group) acquires (L2 invalidate) and forms
+//   out[t, c] = sum_j topk_weights[t, j] * y[t*k + j, c],  j = 0, 1, ... in order
+// for the group's columns, exactly as moe_combine does, then puts the
+// counter back to zero. Which workgroup sums a group does not change its
+// bits, so the result is deterministic. Column tiles start on multiples of
+// 128 and cover whole groups, so every (row, group) is counted once.
+struct CombineArgs {
+    const float* w;      // [T, k] routing weights
+    int32_t* cnt;        // [T, G] arrival counters, zero on entry and on exit
+    void* out;           // [T, N_out] bf16 or fp32
+    int G;               // 128-column groups: ceil(N_out / 128)
+};
+
+constexpr int kCombineGroup = 128;
+
+// Called by every thread of the workgroup after its y stores. row_id(r) is
+// the flat index of row r of the tile (or anything outside [0, n_pairs) for
+// a pad row); list points to LDS for nrows * groups int64 entries plus an
+// int counter.
+template <bool Y16, int OUTF, int THREADS, class RowId>
+__device__ __forceinline__ void combine_completed(RowId row_id, int nrows, int col0, int cols, int k, int64_t n_pairs,
+                                                  int N_out, const void* __restrict__ y, const CombineArgs& ca,
+                                                  int64_t* list, int* n_list, int tid) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    if (tid == 0) *n_list = 0;
+    __syncthreads();
+    const int gpt = cols / kCombineGroup;
+    for (int i = tid; i < nrows * gpt; i += THREADS) {
+        const int r = i / gpt, g = col0 / kCombineGroup + i % gpt;
+        const int64_t id = row_id(r);
+        if (id < 0 || id >= n_pairs || g * kCombineGroup >= N_out) continue;
+        const int64_t e = (id / k) * ca.G + g;
+        if (__hip_atomic_fetch_add(ca.cnt + e, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == k - 1)
+            list[atomicAdd(n_list, 1)] = e;
+    }
+    __syncthreads();
+    const int n = *n_list;
+    if (n == 0) return;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    // 32 threads per completed (token, group), four columns each
+    for (int q = tid / 32; q < n; q += THREADS / 32) {
+        const int64_t e = list[q];
+        const int64_t t = e / ca.G;
+        const int c = (int)(e % ca.G) * kCombineGroup + (tid % 32) * 4;
+        if (c < N_out) {
+            float acc[4] = {0.f, 0.f, 0.f, 0.f};
+            float v[kMaxTopK > 8 ? 8 : kMaxTopK][4];
+            for (int j0 = 0; j0 < k; j0 += 8) {
+                float wj[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const int j = min(j0 + u, k - 1);
+                    wj[u] = ca.w[t * k + j];
+                    const int64_t idx = (t * k + j) * N_out + c;
+                    if constexpr (Y16) {
+                        const uint32_t* p = (const uint32_t*)((const _Float16*)y + idx);
+                        const uint32_t lo = p[0], hi = p[1];
+                        v[u][0] = (float)__builtin_bit_cast(_Float16, (uint16_t)(lo & 0xffffu));
+                        v[u][1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(lo >> 16));
+                        v[u][2] = (float)__builtin_bit_cast(_Float16, (uint16_t)(hi & 0xffffu));
+                        v[u][3] = (float)__builtin_bit_cast(_Float16, (uint16_t)(hi >> 16));
+                    } else {
+                        const f32x4 a = *(const f32x4*)((const float*)y + idx);
+#pragma unroll
+                        for (int m = 0; m < 4; ++m) v[u][m] = a[m];
+                    }
+                }
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const bool use = j0 + u < k;
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) {
+                        const float sum = acc[m] + wj[u] * v[u][m];
+                        acc[m] = use ? sum : acc[m];
+                    }
+                }
+            }
+            if constexpr (OUTF == 2) {
+                *(f32x4*)((float*)ca.out + t * N_out + c) = f32x4{acc[0], acc[1], acc[2], acc[3]};
+            } else {
+                uint32_t* o = (uint32_t*)((uint16_t*)ca.out + t * N_out + c);
+                o[0] = pack_bf16x2(acc[0], acc[1]);
+                o[1] = pack_bf16x2(acc[2], acc[3]);
+            }
+        }
+        if (tid % 32 == 0) ca.cnt[e] = 0;
+    }
+}
+
 template <int BM_, int BN_, bool GATED_>
 struct GemmCfg {
     static constexpr int BM = BM_;
@@ -57,11 +155,11 @@ struct GemmCfg {
     static_assert(!GATED || NT % 2 == 0, "gated tile needs gate and up halves");
 };
 
-template <class C, bool Y16>
+template <class C, bool Y16, int OUTF = 0>
 __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(
     const uint16_t* __restrict__ a_src, const uint16_t* __restrict__ w, const int32_t* __restrict__ sorted_ids,
     const int32_t* __restrict__ block_expert, const int32_t* __restrict__ num_padded, int k, int64_t n_pairs,
-    int K, int N_out, int n_tiles, void* __restrict__ out) {
+    int K, int N_out, int n_tiles, void* __restrict__ out, CombineArgs ca) {
     constexpr int BM = C::BM, BN = C::BN, BK = C::BK, STRIDE = C::STRIDE;
     __shared__ __attribute__((aligned(16))) uint16_t sA[2][BM * STRIDE];
     __shared__ __attribute__((aligned(16))) uint16_t sB[2][BN * BK];  // [band][k-step][512]
@@ -246,6 +344,14 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(
                 }
             }
         }
+        if constexpr (OUTF != 0) {
+            // the stages are free after the k loop's last barrier
+            int64_t* list = (int64_t*)&sA[0][0];
+            int* n_list = (int*)&sB[0][0];
+            static_assert(BM * (BN / kCombineGroup) * 8 <= (int)sizeof(sA[0]), "combine list");
+            combine_completed<Y16, OUTF, C::THREADS>([&](int r) { return row_src[r]; }, BM, tn * BN, BN, k, n_pairs,
+                                                     N_out, out, ca, list, n_list, tid);
+        }
     }
 }
 
@@ -314,11 +420,12 @@ using WideQuarterCfg = WideCfg<false, BM_, 6, 2, 1, 64>;
 // (expert e) against C::BN weight rows from band band0 on, written to the
 // output columns from col0 on. smem holds the stages (and, after the k loop,
 // the epilogue's staging); the caller synchronises before reusing it.
-template <class C, bool Y16>
+template <class C, bool Y16, int OUTF = 0>
 __device__ __forceinline__ void wide_tile(const uint16_t* __restrict__ a_src, const uint16_t* __restrict__ w,
                                           const int32_t* __restrict__ sorted_ids, int e, int mb, int band0,
                                           int col0, int k, int64_t n_pairs, int K, int N_out,
-                                          void* __restrict__ out, char* smem, int tid, int lane, int wave) {
+                                          void* __restrict__ out, char* smem, int tid, int lane, int wave,
+                                          const CombineArgs& ca) {
     constexpr int BM = C::BM, S = C::STAGES;
     const int64_t w_rows = C::GATED ? 2 * (int64_t)N_out : (int64_t)N_out;
     const int bands = (int)(w_rows / 16);
@@ -544,6 +651,13 @@ __device__ __forceinline__ void wide_tile(const uint16_t* __restrict__ a_src, co
             }
             __syncthreads();
         }
+        if constexpr (OUTF != 0) {
+            static_assert(C::COLS % kCombineGroup == 0, "column tiles cover whole combine groups");
+            static_assert(1024 + 16 + BM * (C::COLS / kCombineGroup) * 8 <= C::STAGES * C::STAGE_BYTES, "list");
+            combine_completed<Y16, OUTF, C::THREADS>([&](int r) { return (int64_t)ids_s[r]; }, BM, col0, C::COLS,
+                                                     k, n_pairs, N_out, out, ca, (int64_t*)(stile + 16),
+                                                     (int*)stile, tid);
+        }
     }
 }
 
@@ -559,11 +673,11 @@ __device__ __forceinline__ void wide_tile(const uint16_t* __restrict__ a_src, co
 // AM: grouping blocks per tile row block. With block_m 256 the grouping pads
 // each expert to 256 rows and every 256-row block is computed as two 128-row
 // tiles (AM = 2) of the same expert, so the row block of tile mb is mb / AM.
-template <class C, bool Y16, bool SPLIT, int AM = 1>
+template <class C, bool Y16, bool SPLIT, int AM = 1, int OUTF = 0>
 __global__ __launch_bounds__(C::THREADS) void grouped_gemm_wide_kernel(
     const uint16_t* __restrict__ a_src, const uint16_t* __restrict__ w, const int32_t* __restrict__ sorted_ids,
     const int32_t* __restrict__ block_expert, const int32_t* __restrict__ num_padded, int k, int64_t n_pairs,
-    int K, int N_out, int n_tiles, void* __restrict__ out) {
+    int K, int N_out, int n_tiles, void* __restrict__ out, CombineArgs ca) {
     extern __shared__ __attribute__((aligned(16))) char smem[];
     const int tid = threadIdx.x, lane = tid % kWave;
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // uniform: copy bases and LDS slots in SGPRs
@@ -582,8 +696,8 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_wide_kernel(
         const int tn = (int)(logical % n_tiles), mb = (int)(logical / n_tiles);
         const int e = block_expert[mb / AM];
         if (e < 0) continue;
-        wide_tile<C, Y16>(a_src, w, sorted_ids, e, mb, tn * (C::BN / 16), tn * C::COLS, k, n_pairs, K, N_out, out,
-                          smem, tid, lane, wave);
+        wide_tile<C, Y16, OUTF>(a_src, w, sorted_ids, e, mb, tn * (C::BN / 16), tn * C::COLS, k, n_pairs, K, N_out,
+                                out, smem, tid, lane, wave, ca);
         __syncthreads();  // the next tile's copies reuse the staging memory
     }
     if constexpr (SPLIT) {
@@ -596,16 +710,17 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_wide_kernel(
             const int tn = (int)(logical % n_tiles), mb = (int)(logical / n_tiles);
             const int e = block_expert[mb / AM];
             if (e >= 0)
-                wide_tile<CQ, Y16>(a_src, w, sorted_ids, e, mb, tn * (C::BN / 16) + sub * (CQ::BN / 16),
-                                   tn * C::COLS + sub * CQ::COLS, k, n_pairs, K, N_out, out, smem, tid, lane, wave);
+                wide_tile<CQ, Y16, OUTF>(a_src, w, sorted_ids, e, mb, tn * (C::BN / 16) + sub * (CQ::BN / 16),
+                                         tn * C::COLS + sub * CQ::COLS, k, n_pairs, K, N_out, out, smem, tid, lane,
+                                         wave, ca);
         }
     }
 }
 
-template <class C, bool Y16, int AM = 1>
+template <class C, bool Y16, int AM = 1, int OUTF = 0>
 static int launch_wide(const void* a, const void* w, const int32_t* sorted_ids, const int32_t* block_expert,
                        const int32_t* num_padded, int k, int64_t n_pairs, int K, int N_out, int64_t cap, void* out,
-                       hipStream_t s, const char* what) {
+                       hipStream_t s, const char* what, const CombineArgs& ca = CombineArgs{}) {
     const int n_tiles = (N_out + C::COLS - 1) / C::COLS;
     // The copies take 32-bit offsets: the activation rows they address
     // (gathered x rows, T = n_pairs / k of them, for gate/up; the act rows of
@@ -629,11 +744,11 @@ static int launch_wide(const void* a, const void* w, const int32_t* sorted_ids, 
     constexpr bool SPLIT = !C::GATED;  // quarter tiles for the down projection's last round
     static std::atomic<uint64_t> lds_set{0};
     const int rc =
-        ensure_dynamic_lds((const void*)grouped_gemm_wide_kernel<C, Y16, SPLIT, AM>, (int)lds, lds_set, what);
+        ensure_dynamic_lds((const void*)grouped_gemm_wide_kernel<C, Y16, SPLIT, AM, OUTF>, (int)lds, lds_set, what);
     if (rc) return rc;
-    hipLaunchKernelGGL((grouped_gemm_wide_kernel<C, Y16, SPLIT, AM>), dim3((unsigned)grid), dim3(C::THREADS), lds, s,
-                       (const uint16_t*)a, (const uint16_t*)w, sorted_ids, block_expert, num_padded, k, n_pairs, K,
-                       N_out, n_tiles, out);
+    hipLaunchKernelGGL((grouped_gemm_wide_kernel<C, Y16, SPLIT, AM, OUTF>), dim3((unsigned)grid), dim3(C::THREADS),
+                       lds, s, (const uint16_t*)a, (const uint16_t*)w, sorted_ids, block_expert, num_padded, k,
+                       n_pairs, K, N_out, n_tiles, out, ca);
     return check_launch(what);
 }
 
@@ -650,11 +765,11 @@ static int launch_wide(const void* a, const void* w, const int32_t* sorted_ids, 
 // 65 us); an expert with more row blocks shares them through the caches and
 // keeps ordinary loads (non-temporal there: 13-15% slower at 20 rows per
 // expert).
-template <bool GATED, int NW, int NTILE, int U, bool Y16>
+template <bool GATED, int NW, int NTILE, int U, bool Y16, int OUTF = 0>
 __global__ __launch_bounds__(NW* kWave) void grouped_gemm_skinny_kernel(
     const uint16_t* __restrict__ a_src, const uint16_t* __restrict__ w, const int32_t* __restrict__ sorted_ids,
     const int32_t* __restrict__ block_expert, const int32_t* __restrict__ num_padded, int k, int64_t n_pairs,
-    int K, int N_out, int n_tiles, void* __restrict__ out) {
+    int K, int N_out, int n_tiles, void* __restrict__ out, CombineArgs ca) {
     constexpr int BM = 16;
     constexpr int COLS = GATED ? 8 * NTILE : 16 * NTILE;  // output columns per wave
     static_assert(!GATED || NTILE % 2 == 0, "gate/up needs gate and up tiles in pairs");
@@ -767,71 +882,84 @@ __global__ __launch_bounds__(NW* kWave) void grouped_gemm_skinny_kernel(
                 if (col < N_out) store_y<Y16>(out, (int64_t)dst * N_out + col, acc[j][q]);
             }
         }
+        if constexpr (OUTF != 0) {
+            constexpr int WG_COLS = NW * COLS;
+            static_assert(WG_COLS % kCombineGroup == 0, "column tiles cover whole combine groups");
+            __shared__ int64_t list[BM * (WG_COLS / kCombineGroup)];
+            __shared__ int n_list;
+            const int32_t* ids = sorted_ids + (int64_t)mb * BM;
+            combine_completed<Y16, OUTF, NW * kWave>([&](int r) { return (int64_t)ids[r]; }, BM, tn * WG_COLS,
+                                                     WG_COLS, k, n_pairs, N_out, out, ca, list, &n_list,
+                                                     (int)threadIdx.x);
+        }
     }
 }
 
-template <bool GATED, int NW, int NTILE, int U, bool Y16>
+template <bool GATED, int NW, int NTILE, int U, bool Y16, int OUTF>
 static int launch_skinny_cfg(const void* a, const void* w, const int32_t* sorted_ids, const int32_t* block_expert,
                              const int32_t* num_padded, int k, int64_t n_pairs, int K, int N_out, int64_t cap,
-                             void* out, hipStream_t s, const char* what) {
+                             void* out, hipStream_t s, const char* what, const CombineArgs& ca) {
     const int cols_per_wg = NW * (GATED ? 8 * NTILE : 16 * NTILE);
     const int n_tiles = (N_out + cols_per_wg - 1) / cols_per_wg;
     const int64_t grid = (cap / 16) * n_tiles;
     if (grid >= ((int64_t)1 << 31)) return set_error(MOE_ERR_UNSUPPORTED, "%s: grid too large", what);
-    hipLaunchKernelGGL((grouped_gemm_skinny_kernel<GATED, NW, NTILE, U, Y16>), dim3((unsigned)grid), dim3(NW * kWave), 0,
-                       s, (const uint16_t*)a, (const uint16_t*)w, sorted_ids, block_expert, num_padded, k, n_pairs, K,
-                       N_out, n_tiles, out);
+    hipLaunchKernelGGL((grouped_gemm_skinny_kernel<GATED, NW, NTILE, U, Y16, OUTF>), dim3((unsigned)grid),
+                       dim3(NW * kWave), 0, s, (const uint16_t*)a, (const uint16_t*)w, sorted_ids, block_expert,
+                       num_padded, k, n_pairs, K, N_out, n_tiles, out, ca);
     return check_launch(what);
 }
 
-template <bool GATED, bool Y16>
+template <bool GATED, bool Y16, int OUTF>
 static int launch_skinny(const void* a, const void* w, const int32_t* sorted_ids, const int32_t* block_expert,
                          const int32_t* num_padded, int k, int64_t n_pairs, int K, int N_out, int64_t cap, void* out,
-                         hipStream_t s, const char* what) {
+                         hipStream_t s, const char* what, const CombineArgs& ca) {
     // Chosen by sweeps on the decode-shaped layer: single-wave workgroups
     // (finest load balance) for gate/up; the down shape is insensitive.
     if (GATED)
-        return launch_skinny_cfg<true, 1, 2, 8, false>(a, w, sorted_ids, block_expert, num_padded, k, n_pairs, K, N_out, cap,
-                                                out, s, what);
-    return launch_skinny_cfg<false, 4, 4, 4, Y16>(a, w, sorted_ids, block_expert, num_padded, k, n_pairs, K, N_out, cap,
-                                             out, s, what);
+        return launch_skinny_cfg<true, 1, 2, 8, false, 0>(a, w, sorted_ids, block_expert, num_padded, k, n_pairs, K,
+                                                          N_out, cap, out, s, what, ca);
+    return launch_skinny_cfg<false, 4, 4, 4, Y16, OUTF>(a, w, sorted_ids, block_expert, num_padded, k, n_pairs, K,
+                                                        N_out, cap, out, s, what, ca);
 }
 
-template <class C, bool Y16>
+template <class C, bool Y16, int OUTF>
 static int launch_gemm(const void* a, const void* w, const int32_t* sorted_ids, const int32_t* block_expert,
                        const int32_t* num_padded, int k, int64_t n_pairs, int K, int N_out, int64_t cap, void* out,
-                       hipStream_t s, const char* what) {
+                       hipStream_t s, const char* what, const CombineArgs& ca) {
     const int n_cols = C::GATED ? C::BN / 2 : C::BN;
     const int n_tiles = (N_out + n_cols - 1) / n_cols;
     const int64_t m_blocks = cap / C::BM;
     const int64_t grid = m_blocks * n_tiles;
     if (grid >= ((int64_t)1 << 31)) return set_error(MOE_ERR_UNSUPPORTED, "%s: grid too large", what);
-    hipLaunchKernelGGL((grouped_gemm_kernel<C, Y16>), dim3((unsigned)grid), dim3(C::THREADS), 0, s, (const uint16_t*)a,
-                       (const uint16_t*)w, sorted_ids, block_expert, num_padded, k, n_pairs, K, N_out, n_tiles,
-                       out);
+    hipLaunchKernelGGL((grouped_gemm_kernel<C, Y16, OUTF>), dim3((unsigned)grid), dim3(C::THREADS), 0, s,
+                       (const uint16_t*)a, (const uint16_t*)w, sorted_ids, block_expert, num_padded, k, n_pairs, K,
+                       N_out, n_tiles, out, ca);
     return check_launch(what);
 }
 
-template <bool GATED, bool Y16>
+// OUTF: 0 = plain projection (y only); 1 / 2 = the weighted combine fused in,
+// out bf16 / fp32 (down projection only).
+template <bool GATED, bool Y16, int OUTF = 0>
 static int dispatch_gemm(int32_t block_m, const void* a, const void* w, const int32_t* sorted_ids,
                          const int32_t* block_expert, const int32_t* num_padded, int k, int64_t n_pairs, int K,
-                         int N_out, int64_t cap, void* out, hipStream_t s, const char* what) {
+                         int N_out, int64_t cap, void* out, hipStream_t s, const char* what,
+                         const CombineArgs& ca = CombineArgs{}) {
     switch (block_m) {
         case 16:
-            return launch_skinny<GATED, Y16>(a, w, sorted_ids, block_expert, num_padded, k, n_pairs, K, N_out, cap, out, s,
-                                        what);
+            return launch_skinny<GATED, Y16, OUTF>(a, w, sorted_ids, block_expert, num_padded, k, n_pairs, K, N_out,
+                                                   cap, out, s, what, ca);
         case 32:
-            return launch_gemm<GemmCfg<32, 128, GATED>, Y16>(a, w, sorted_ids, block_expert, num_padded, k, n_pairs, K,
-                                                       N_out, cap, out, s, what);
+            return launch_gemm<GemmCfg<32, 128, GATED>, Y16, OUTF>(a, w, sorted_ids, block_expert, num_padded, k,
+                                                                   n_pairs, K, N_out, cap, out, s, what, ca);
         case 64:
-            return launch_wide<WideCfg<GATED, 64, 4>, Y16>(a, w, sorted_ids, block_expert, num_padded, k, n_pairs, K,
-                                                      N_out, cap, out, s, what);
+            return launch_wide<WideCfg<GATED, 64, 4>, Y16, 1, OUTF>(a, w, sorted_ids, block_expert, num_padded, k,
+                                                                    n_pairs, K, N_out, cap, out, s, what, ca);
         case 128:
-            return launch_wide<WideCfg<GATED, 128, GATED ? 4 : 3>, Y16>(a, w, sorted_ids, block_expert, num_padded, k, n_pairs, K,
-                                                       N_out, cap, out, s, what);
+            return launch_wide<WideCfg<GATED, 128, GATED ? 4 : 3>, Y16, 1, OUTF>(
+                a, w, sorted_ids, block_expert, num_padded, k, n_pairs, K, N_out, cap, out, s, what, ca);
         case 256:  // two 128-row tiles per grouping block: the same bits as block_m 128 for every row
-            return launch_wide<WideCfg<GATED, 128, GATED ? 4 : 3>, Y16, 2>(a, w, sorted_ids, block_expert, num_padded,
-                                                                          k, n_pairs, K, N_out, cap, out, s, what);
+            return launch_wide<WideCfg<GATED, 128, GATED ? 4 : 3>, Y16, 2, OUTF>(
+                a, w, sorted_ids, block_expert, num_padded, k, n_pairs, K, N_out, cap, out, s, what, ca);
     }
     return set_error(MOE_ERR_UNSUPPORTED, "%s: block_m=%d not in {16,32,64,128,256}", what, block_m);
 }
@@ -887,6 +1015,43 @@ extern "C" int moe_grouped_gemm_down(const void* act, const void* w2, const int3
                                           y, (hipStream_t)stream, fn);
     return dispatch_gemm<false, false>(block_m, act, w2, sorted_ids, block_expert, num_padded, k, T * k, I, H, cap, y,
                                        (hipStream_t)stream, fn);
+}
+
+extern "C" int64_t moe_combine_counter_count(int64_t T, int32_t H) {
+    if (T < 0 || H <= 0) return -1;
+    return T * ((H + moe::kCombineGroup - 1) / moe::kCombineGroup);
+}
+
+extern "C" int moe_grouped_gemm_down_combine(const void* act, const void* w2, const int32_t* sorted_ids,
+                                             const int32_t* block_expert, const int32_t* num_padded,
+                                             const float* topk_weights, int64_t T, int32_t k, int32_t H, int32_t I,
+                                             int32_t E, int32_t block_m, int64_t cap, void* y, int32_t y_dtype,
+                                             int32_t* counters, void* out, int32_t out_dtype, void* stream) {
+    using namespace moe;
+    clear_error();
+    const char* fn = "moe_grouped_gemm_down_combine";
+    if (y_dtype != MOE_DTYPE_FP16 && y_dtype != MOE_DTYPE_FP32)
+        return set_error(MOE_ERR_INVALID, "%s: y_dtype=%d is neither fp16 (2) nor fp32 (1)", fn, y_dtype);
+    if (out_dtype != MOE_OUT_BF16 && out_dtype != MOE_OUT_FP32)
+        return set_error(MOE_ERR_INVALID, "%s: out_dtype=%d is neither bf16 (0) nor fp32 (1)", fn, out_dtype);
+    int rc = check_gemm_args(fn, act, w2, sorted_ids, block_expert, num_padded, T, k, H, I, E, block_m, cap, y);
+    if (rc || T == 0) return rc;
+    if (!topk_weights || !counters || !out) return set_error(MOE_ERR_INVALID, "%s: required pointer is NULL", fn);
+    if ((uintptr_t)out & 15) return set_error(MOE_ERR_INVALID, "%s: out must be 16-byte aligned", fn);
+    const CombineArgs ca{topk_weights, counters, out, (H + kCombineGroup - 1) / kCombineGroup};
+    hipStream_t s = (hipStream_t)stream;
+    const bool y16 = y_dtype == MOE_DTYPE_FP16, o32 = out_dtype == MOE_OUT_FP32;
+    if (y16 && o32)
+        return dispatch_gemm<false, true, 2>(block_m, act, w2, sorted_ids, block_expert, num_padded, k, T * k, I, H, cap,
+                                             y, s, fn, ca);
+    if (y16)
+        return dispatch_gemm<false, true, 1>(block_m, act, w2, sorted_ids, block_expert, num_padded, k, T * k, I, H, cap,
+                                             y, s, fn, ca);
+    if (o32)
+        return dispatch_gemm<false, false, 2>(block_m, act, w2, sorted_ids, block_expert, num_padded, k, T * k, I, H,
+                                              cap, y, s, fn, ca);
+    return dispatch_gemm<false, false, 1>(block_m, act, w2, sorted_ids, block_expert, num_padded, k, T * k, I, H, cap,
+                                          y, s, fn, ca);
 }
 
 extern "C" int32_t moe_pick_block_m(int64_t T, int32_t k, int32_t E) {

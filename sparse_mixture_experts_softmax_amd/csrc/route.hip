@@ -24,16 +24,79 @@ constexpr int kRouteTokens = 16;  // tokens per logits tile (the MFMA M size)
 constexpr int kRouteSlices = 4;   // waves per logits workgroup = slices of H
 constexpr int kTopkWaves = 4;     // tokens per top-k workgroup
 
-template <int NTW, int U>
+// The residual add + RMSNorm that precedes the layer, fused into the
+// router's read of x (moe_fused_add_rmsnorm_route): the router kernels then
+// read x and the residual, form the new residual r = bf16(residual + x) (or
+// x for the first layer), the row's inv = 1 / sqrt(mean(r^2) + eps) and the
+// normalized row bf16(w * bf16(r * inv)), multiply that with the router
+// weight, and the workgroups of the first expert tile write r and the
+// normalized row out. Every router workgroup of a token block reads the
+// block's rows, so the outputs go to other buffers than the inputs.
+struct NormArgs {
+    const uint16_t* res;  // [T, H] residual in (ignored without has_res)
+    const uint16_t* w;    // [H] norm weight
+    uint16_t* x_out;      // [T, H] normalized x
+    uint16_t* res_out;    // [T, H] new residual
+    float eps;
+    int has_res;
+};
+
+// New residual of one 16-byte chunk: bf16(fp32(res) + fp32(x)), or x.
+__device__ __forceinline__ u32x4 new_residual(u32x4 xv, u32x4 rv, int has_res) {
+    if (!has_res) return xv;
+    u32x4 o;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const float lo = __uint_as_float(rv[q] << 16) + __uint_as_float(xv[q] << 16);
+        const float hi = __uint_as_float(rv[q] & 0xffff0000u) + __uint_as_float(xv[q] & 0xffff0000u);
+        o[q] = pack_bf16x2(lo, hi);
+    }
+    return o;
+}
+
+// Adds the squares of a chunk's eight values to ss, in element order.
+__device__ __forceinline__ float add_squares(float ss, u32x4 r) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const float lo = __uint_as_float(r[q] << 16), hi = __uint_as_float(r[q] & 0xffff0000u);
+        ss += lo * lo;
+        ss += hi * hi;
+    }
+    return ss;
+}
+
+// bf16(w * bf16(r * inv)) of one chunk (the weight product of two bf16
+// values is exact in fp32 and rounded once).
+__device__ __forceinline__ u32x4 normalized(u32x4 r, u32x4 w, float inv) {
+    u32x4 o;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const float n0 = bf16_to_f32(f32_to_bf16(__uint_as_float(r[q] << 16) * inv));
+        const float n1 = bf16_to_f32(f32_to_bf16(__uint_as_float(r[q] & 0xffff0000u) * inv));
+        o[q] = pack_bf16x2(__uint_as_float(w[q] << 16) * n0, __uint_as_float(w[q] & 0xffff0000u) * n1);
+    }
+    return o;
+}
+
+// Sum of a lane's squares over the four lanes holding the same row (lanes
+// l, l^16, l^32, l^48): every lane receives its row's total.
+__device__ __forceinline__ float row_total(float ss) {
+    ss += wave_shfl_xor(ss, 16);
+    ss += wave_shfl_xor(ss, 32);
+    return ss;
+}
+
+template <int NTW, int U, bool NORM>
 __global__ __launch_bounds__(kRouteSlices* kWave) void router_logits_kernel(const uint16_t* __restrict__ x,
                                                                             const uint16_t* __restrict__ wr,
                                                                             const float* __restrict__ bias,
                                                                             float* __restrict__ logits, int64_t T,
-                                                                            int H, int E) {
+                                                                            int H, int E, NormArgs na) {
     // U: k-steps per batch of loads (all loads of a batch are issued before
     // the first MFMA: one memory wait per batch)
     constexpr int COLS = 16 * NTW;
     __shared__ float part[kRouteSlices][kRouteTokens][COLS + 1];
+    __shared__ float part_ss[kRouteSlices][kRouteTokens];
     const int lane = threadIdx.x % kWave, slice = threadIdx.x / kWave;
     const int64_t t0 = (int64_t)blockIdx.x * kRouteTokens;
     const int e0 = blockIdx.y * COLS;
@@ -41,7 +104,8 @@ __global__ __launch_bounds__(kRouteSlices* kWave) void router_logits_kernel(cons
     const bool row_ok = t0 + row < T;
     // unconditional loads from clamped rows: rows past T are zeroed, experts
     // past E only feed logits that are never stored
-    const uint16_t* xrow = x + (row_ok ? (t0 + row) * (int64_t)H : 0) + koff;
+    const int64_t xoff = (row_ok ? (t0 + row) * (int64_t)H : 0) + koff;
+    const uint16_t* xrow = x + xoff;
     const uint16_t* wrow[NTW];
 #pragma unroll
     for (int n = 0; n < NTW; ++n) wrow[n] = wr + (int64_t)min(e0 + n * 16 + row, E - 1) * H + koff;
@@ -51,22 +115,74 @@ __global__ __launch_bounds__(kRouteSlices* kWave) void router_logits_kernel(cons
     const int ksteps = H / 32;
     const int per = (ksteps + kRouteSlices - 1) / kRouteSlices;
     const int s_lo = slice * per, s_hi = min(ksteps, s_lo + per);
+
+    float inv = 0.f;
+    const uint16_t* rrow = nullptr;
+    const bool writer = NORM && blockIdx.y == 0 && row_ok;
+    if constexpr (NORM) {
+        // pass 1: the row's sum of squares of the new residual (this wave's
+        // slice, k-step by k-step, then the four lanes of a row, then the
+        // four slices in order)
+        rrow = na.has_res ? na.res + xoff : xrow;
+        float ss = 0.f;
+        int s = s_lo;
+        for (; s + U <= s_hi; s += U) {
+            u32x4 xv[U], rv[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                xv[u] = ld16(xrow + (s + u) * 32);
+                rv[u] = ld16(rrow + (s + u) * 32);
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) ss = add_squares(ss, new_residual(xv[u], rv[u], na.has_res));
+        }
+        for (; s < s_hi; ++s) ss = add_squares(ss, new_residual(ld16(xrow + s * 32), ld16(rrow + s * 32), na.has_res));
+        ss = row_total(ss);
+        if (lane < 16) part_ss[slice][row] = ss;
+        __syncthreads();
+        float tot = 0.f;
+#pragma unroll
+        for (int sl = 0; sl < kRouteSlices; ++sl) tot += part_ss[sl][row];
+        inv = 1.0f / sqrtf(tot / (float)H + na.eps);
+    }
+    // A operand of k-step s: the x chunk, or (fused norm) its normalized
+    // value, written out with the new residual by the first expert tile
+    auto a_chunk = [&](u32x4 xv, u32x4 rv, u32x4 wv, int s_) -> u32x4 {
+        if constexpr (!NORM) {
+            return sel(row_ok, xv);
+        } else {
+            const u32x4 r = new_residual(xv, rv, na.has_res);
+            const u32x4 xn = normalized(r, wv, inv);
+            if (writer) {
+                *(u32x4*)(na.res_out + xoff + s_ * 32) = r;
+                *(u32x4*)(na.x_out + xoff + s_ * 32) = xn;
+            }
+            return sel(row_ok, xn);
+        }
+    };
     int s = s_lo;
     for (; s + U <= s_hi; s += U) {
-        u32x4 a[U], b[U][NTW];
+        u32x4 a[U], b[U][NTW], rv[U], wv[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            a[u] = sel(row_ok, ld16(xrow + (s + u) * 32));
+            a[u] = ld16(xrow + (s + u) * 32);
+            if constexpr (NORM) {
+                rv[u] = ld16(rrow + (s + u) * 32);
+                wv[u] = ld16(na.w + (s + u) * 32 + koff);
+            }
 #pragma unroll
             for (int n = 0; n < NTW; ++n) b[u][n] = ld16(wrow[n] + (s + u) * 32);
         }
 #pragma unroll
-        for (int u = 0; u < U; ++u)
+        for (int u = 0; u < U; ++u) {
+            const u32x4 au = a_chunk(a[u], NORM ? rv[u] : a[u], NORM ? wv[u] : a[u], s + u);
 #pragma unroll
-            for (int n = 0; n < NTW; ++n) acc[n] = mfma16x16x32(a[u], b[u][n], acc[n]);
+            for (int n = 0; n < NTW; ++n) acc[n] = mfma16x16x32(au, b[u][n], acc[n]);
+        }
     }
     for (; s < s_hi; ++s) {
-        const u32x4 a = sel(row_ok, ld16(xrow + s * 32));
+        const u32x4 xv = ld16(xrow + s * 32);
+        const u32x4 a = a_chunk(xv, NORM ? ld16(rrow + s * 32) : xv, NORM ? ld16(na.w + s * 32 + koff) : xv, s);
 #pragma unroll
         for (int n = 0; n < NTW; ++n) acc[n] = mfma16x16x32(a, ld16(wrow[n] + s * 32), acc[n]);
     }
@@ -104,27 +220,45 @@ __global__ __launch_bounds__(kRouteSlices* kWave) void router_logits_kernel(cons
 constexpr int kRouteWideTokens = 64;
 constexpr int kRouteChunk = 4;  // k-steps per chunk (RC)
 
-template <int ET, int NB_>
+// s_waitcnt until at most `later` chunks of OPS copies each remain in
+// flight (later <= L; only the waits that can occur are instantiated).
+template <int L, int OPS>
+__device__ __forceinline__ void wait_for_later(int later) {
+    if constexpr (L > 0) {
+        if (later >= L) {
+            vm_wait<L * OPS>();
+            return;
+        }
+        wait_for_later<L - 1, OPS>(later);
+    } else {
+        vm_wait<0>();
+    }
+}
+
+// With NORM (the fused residual add + RMSNorm), each chunk also holds the
+// wave's residual fragments next to its activation fragments, and the norm
+// weight is staged in LDS (H*2 bytes after the ring) once per workgroup.
+template <int ET, int NB_, bool NORM = false>
 struct RouteWide {
     static constexpr int RC = kRouteChunk, NB = NB_, D = NB - 1;
     static constexpr int W_COPIES = ET * RC / kRouteSlices;  // router fragments per wave per chunk
-    static constexpr int X_COPIES = RC;                      // activation fragments per wave per chunk
+    static constexpr int X_COPIES = RC * (NORM ? 2 : 1);     // activation (+ residual) fragments per wave per chunk
     static constexpr int OPS = W_COPIES + X_COPIES;
     static constexpr int W_BYTES = ET * RC * 1024;
     static constexpr int X_BYTES = kRouteSlices * RC * 1024;
-    static constexpr int CHUNK_BYTES = W_BYTES + X_BYTES;
+    static constexpr int CHUNK_BYTES = W_BYTES + X_BYTES * (NORM ? 2 : 1);
     static_assert((ET * RC) % kRouteSlices == 0, "router fragments split evenly over the waves");
     static_assert(OPS * (D - 1) < 64, "vmcnt range");
     static_assert(NB * CHUNK_BYTES <= 160 * 1024, "LDS");
 };
 
-template <int ET, int NB_>
+template <int ET, int NB_, bool NORM>
 __global__ __launch_bounds__(kRouteSlices* kWave) void router_logits_wide_kernel(const uint16_t* __restrict__ x,
                                                                                  const uint16_t* __restrict__ wr,
                                                                                  const float* __restrict__ bias,
                                                                                  float* __restrict__ logits,
-                                                                                 int64_t T, int H, int E) {
-    using C = RouteWide<ET, NB_>;
+                                                                                 int64_t T, int H, int E, NormArgs na) {
+    using C = RouteWide<ET, NB_, NORM>;
     constexpr int RC = C::RC, NB = C::NB, D = C::D;
     extern __shared__ __attribute__((aligned(16))) char smem[];
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
@@ -133,7 +267,10 @@ __global__ __launch_bounds__(kRouteSlices* kWave) void router_logits_wide_kernel
     const int row = lane % 16, koff = (lane / 16) * 8;
     // unconditional copies from clamped rows: rows past T are never stored,
     // experts past E only feed logits that are never stored
-    const uint16_t* xsrc = x + min(t0 + row, T - 1) * (int64_t)H + koff;
+    const int64_t xoff = min(t0 + row, T - 1) * (int64_t)H + koff;
+    const uint16_t* xsrc = x + xoff;
+    const uint16_t* rsrc = NORM ? (na.has_res ? na.res + xoff : xsrc) : nullptr;
+    const bool writer = NORM && blockIdx.y == 0 && t0 + row < T;
     const uint16_t* wsrc[C::W_COPIES];
     int wdst[C::W_COPIES];
 #pragma unroll
@@ -149,6 +286,11 @@ __global__ __launch_bounds__(kRouteSlices* kWave) void router_logits_wide_kernel
         for (int j = 0; j < C::W_COPIES; ++j) lds_dma16(wsrc[j] + c * RC * 32, buf + wdst[j]);
 #pragma unroll
         for (int s = 0; s < RC; ++s) lds_dma16(xsrc + (c * RC + s) * 32, buf + C::W_BYTES + (wave * RC + s) * 1024);
+        if constexpr (NORM) {
+#pragma unroll
+            for (int s = 0; s < RC; ++s)
+                lds_dma16(rsrc + (c * RC + s) * 32, buf + C::W_BYTES + C::X_BYTES + (wave * RC + s) * 1024);
+        }
     };
     f32x4 acc[kRouteSlices][ET];
 #pragma unroll
@@ -157,6 +299,37 @@ __global__ __launch_bounds__(kRouteSlices* kWave) void router_logits_wide_kernel
         for (int j = 0; j < ET; ++j) acc[sl][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     for (int c = 0; c < D && c < nchunk; ++c) issue(c);
+    float inv = 0.f;
+    uint16_t* w_lds = (uint16_t*)(smem + NB * C::CHUNK_BYTES);
+    if constexpr (NORM) {
+        // the norm weight, once, into LDS
+        for (int h = tid * 8; h < H; h += kRouteSlices * kWave * 8) *(u32x4*)(w_lds + h) = ld16(na.w + h);
+        // the row's sum of squares of the new residual, per slice of H and
+        // in the small-batch kernel's order (k-step by k-step in a lane, the
+        // four lanes of a row, then the slices in order), so both kernels
+        // normalize a row with the same inv
+        float tot = 0.f;
+        for (int sl = 0; sl < kRouteSlices; ++sl) {
+            float ss = 0.f;
+            constexpr int B8 = 8;
+            int s = sl * per;
+            for (; s + B8 <= (sl + 1) * per; s += B8) {
+                u32x4 xv[B8], rv[B8];
+#pragma unroll
+                for (int u = 0; u < B8; ++u) {
+                    xv[u] = ld16(xsrc + (s + u) * 32);
+                    rv[u] = ld16(rsrc + (s + u) * 32);
+                }
+#pragma unroll
+                for (int u = 0; u < B8; ++u) ss = add_squares(ss, new_residual(xv[u], rv[u], na.has_res));
+            }
+            for (; s < (sl + 1) * per; ++s)
+                ss = add_squares(ss, new_residual(ld16(xsrc + s * 32), ld16(rsrc + s * 32), na.has_res));
+            tot += row_total(ss);
+        }
+        inv = 1.0f / sqrtf(tot / (float)H + na.eps);
+        __syncthreads();  // the norm weight is in LDS
+    }
     int c = 0;
 #pragma unroll
     for (int sl = 0; sl < kRouteSlices; ++sl) {
@@ -166,17 +339,23 @@ __global__ __launch_bounds__(kRouteSlices* kWave) void router_logits_wide_kernel
             // the chunk and frees the buffer of chunk c - 1
             const int later = min(D - 1, nchunk - 1 - c);
             static_assert(D <= 5, "wait ladder covers up to four later chunks");
-            if (later >= 4) vm_wait<4 * C::OPS>();
-            else if (later == 3) vm_wait<3 * C::OPS>();
-            else if (later == 2) vm_wait<2 * C::OPS>();
-            else if (later == 1) vm_wait<C::OPS>();
-            else vm_wait<0>();
+            wait_for_later<D - 1, C::OPS>(later);
             __builtin_amdgcn_s_barrier();
             if (c + D < nchunk) issue(c + D);
             const char* buf = smem + (c % NB) * C::CHUNK_BYTES;
 #pragma unroll
             for (int s = 0; s < RC; ++s) {
-                const u32x4 a = *(const u32x4*)(buf + C::W_BYTES + (wave * RC + s) * 1024 + lane * 16);
+                u32x4 a = *(const u32x4*)(buf + C::W_BYTES + (wave * RC + s) * 1024 + lane * 16);
+                if constexpr (NORM) {
+                    const int ks = c * RC + s;
+                    const u32x4 rv = *(const u32x4*)(buf + C::W_BYTES + C::X_BYTES + (wave * RC + s) * 1024 + lane * 16);
+                    const u32x4 r = new_residual(a, rv, na.has_res);
+                    a = normalized(r, *(const u32x4*)(w_lds + ks * 32 + koff), inv);
+                    if (writer) {
+                        *(u32x4*)(na.res_out + xoff + ks * 32) = r;
+                        *(u32x4*)(na.x_out + xoff + ks * 32) = a;
+                    }
+                }
 #pragma unroll
                 for (int j = 0; j < ET; ++j)
                     acc[sl][j] = mfma16x16x32(a, *(const u32x4*)(buf + (j * RC + s) * 1024 + lane * 16), acc[sl][j]);
@@ -401,77 +580,66 @@ __global__ __launch_bounds__(kTopkWaves* kWave) void route_topk_row_kernel(const
     }
 }
 
-template <int ET, int NB>
+template <int ET, int NB, bool NORM>
 static int launch_route_wide(const void* x, const void* w_router, const float* bias, float* logits, int64_t T,
-                             int32_t H, int32_t E, int ntiles, hipStream_t s) {
+                             int32_t H, int32_t E, int ntiles, const NormArgs& na, hipStream_t s) {
+    using C = RouteWide<ET, NB, NORM>;
     const dim3 grid((unsigned)((T + kRouteWideTokens - 1) / kRouteWideTokens), (unsigned)((ntiles + ET - 1) / ET));
-    constexpr int lds = RouteWide<ET, NB>::NB * RouteWide<ET, NB>::CHUNK_BYTES;
+    const int lds = C::NB * C::CHUNK_BYTES + (NORM ? H * 2 : 0);
+    if (lds > 160 * 1024) return set_error(MOE_ERR_UNSUPPORTED, "moe_route: H=%d too large for the fused norm", H);
     static std::atomic<uint64_t> lds_set{0};
-    const int rc = ensure_dynamic_lds((const void*)router_logits_wide_kernel<ET, NB>, lds, lds_set, "moe_route");
+    const int rc = ensure_dynamic_lds((const void*)router_logits_wide_kernel<ET, NB, NORM>,
+                                      NORM ? 160 * 1024 : lds, lds_set, "moe_route");
     if (rc) return rc;
-    hipLaunchKernelGGL((router_logits_wide_kernel<ET, NB>), grid, dim3(kRouteSlices * kWave), lds, s,
-                       (const uint16_t*)x, (const uint16_t*)w_router, bias, logits, T, (int)H, (int)E);
+    hipLaunchKernelGGL((router_logits_wide_kernel<ET, NB, NORM>), grid, dim3(kRouteSlices * kWave), lds, s,
+                       (const uint16_t*)x, (const uint16_t*)w_router, bias, logits, T, (int)H, (int)E, na);
     return MOE_OK;
 }
 
-}  // namespace moe
-
-extern "C" int moe_route(const void* x, const void* w_router, const float* router_bias, float* logits,
-                         int32_t* topk_ids, float* topk_weights, int64_t T, int32_t H, int32_t E, int32_t k,
-                         int32_t norm_topk_prob, void* stream) {
-    using namespace moe;
-    clear_error();
-    if (x == nullptr) {
-        // logits are an input; H is not used
-        if (T < 0 || E < 0 || k < 0) return set_error(MOE_ERR_INVALID, "moe_route: negative size");
-        if (E < 1 || E > kMaxExperts) return set_error(MOE_ERR_UNSUPPORTED, "moe_route: E=%d outside [1, 256]", E);
-        if (k < 1 || k > E || k > kMaxTopK) return set_error(MOE_ERR_UNSUPPORTED, "moe_route: k=%d invalid", k);
-        if (T * (int64_t)k >= ((int64_t)1 << 31)) return set_error(MOE_ERR_UNSUPPORTED, "moe_route: T*k too large");
+// Router logits (a1), optionally with the residual add + RMSNorm fused into
+// the read of x (na != nullptr), then the softmax / top-k (a2). Arguments
+// are checked by the callers.
+template <bool NORM>
+static int route_logits(const void* x, const void* w_router, const float* router_bias, float* logits, int64_t T,
+                        int32_t H, int32_t E, const NormArgs& na, hipStream_t s) {
+    const int64_t tblocks = (T + kRouteTokens - 1) / kRouteTokens;
+    const int ntiles = (E + 15) / 16;
+    if (tblocks >= ((int64_t)1 << 31)) return set_error(MOE_ERR_UNSUPPORTED, "moe_route: T too large");
+    const int ksteps = H / 32;
+    if (T > 256 && ksteps % (kRouteSlices * kRouteChunk) == 0) {
+        // Each workgroup re-reads its 64 activation rows once per group of
+        // 16*ET experts, so ET is as large as still gives a full round of
+        // workgroups on the 256 CUs (one per CU, the deepest ring); below
+        // that, ET = 2 with a shallower ring, two per CU. With the fused
+        // norm each chunk also carries the residual, so the rings are one
+        // or two chunks shallower.
+        const int64_t tg = (T + kRouteWideTokens - 1) / kRouteWideTokens;
+        int rc;
+        if (tg * ((ntiles + 7) / 8) >= 256)
+            rc = launch_route_wide<8, NORM ? 2 : 3, NORM>(x, w_router, router_bias, logits, T, H, E, ntiles, na, s);
+        else if (tg * ((ntiles + 3) / 4) >= 256)
+            rc = launch_route_wide<4, NORM ? 2 : 4, NORM>(x, w_router, router_bias, logits, T, H, E, ntiles, na, s);
+        else if (tg * ((ntiles + 1) / 2) <= 256)
+            rc = launch_route_wide<2, NORM ? 3 : 6, NORM>(x, w_router, router_bias, logits, T, H, E, ntiles, na, s);
+        else
+            rc = launch_route_wide<2, 3, NORM>(x, w_router, router_bias, logits, T, H, E, ntiles, na, s);
+        if (rc) return rc;
+    } else if (T <= 256 || ntiles < 8) {
+        // one batch of loads per slice at H = 2048 (16 k-steps; 8 with the
+        // fused norm, which also holds the residual and norm weight chunks)
+        hipLaunchKernelGGL((router_logits_kernel<1, NORM ? 8 : 16, NORM>), dim3((unsigned)tblocks, (unsigned)ntiles),
+                           dim3(kRouteSlices * kWave), 0, s, (const uint16_t*)x, (const uint16_t*)w_router,
+                           router_bias, logits, T, (int)H, (int)E, na);
     } else {
-        int rc = check_shape("moe_route", T, H, E, k, -1);
-        if (rc) return rc;
-        if (!w_router) return set_error(MOE_ERR_INVALID, "moe_route: w_router is NULL");
+        hipLaunchKernelGGL((router_logits_kernel<8, NORM ? 4 : 8, NORM>),
+                           dim3((unsigned)tblocks, (unsigned)((ntiles + 7) / 8)), dim3(kRouteSlices * kWave), 0, s,
+                           (const uint16_t*)x, (const uint16_t*)w_router, router_bias, logits, T, (int)H, (int)E, na);
     }
-    if (T == 0) return MOE_OK;
-    if (!logits || !topk_ids || !topk_weights)
-        return set_error(MOE_ERR_INVALID, "moe_route: logits/topk_ids/topk_weights must not be NULL");
-    if (x && (((uintptr_t)x | (uintptr_t)w_router) & 15))
-        return set_error(MOE_ERR_INVALID, "moe_route: x and w_router must be 16-byte aligned");
-    hipStream_t s = (hipStream_t)stream;
-    if (x) {
-        const int64_t tblocks = (T + kRouteTokens - 1) / kRouteTokens;
-        const int ntiles = (E + 15) / 16;
-        if (tblocks >= ((int64_t)1 << 31)) return set_error(MOE_ERR_UNSUPPORTED, "moe_route: T too large");
-        const int ksteps = H / 32;
-        if (T > 256 && ksteps % (kRouteSlices * kRouteChunk) == 0) {
-            // Each workgroup re-reads its 64 activation rows once per group
-            // of 16*ET experts, so ET is as large as still gives a full round
-            // of workgroups on the 256 CUs (one per CU, the deepest ring);
-            // below that, ET = 2 with a shallower ring, two per CU.
-            const int64_t tg = (T + kRouteWideTokens - 1) / kRouteWideTokens;
-            int rc;
-            if (tg * ((ntiles + 7) / 8) >= 256)
-                rc = launch_route_wide<8, 3>(x, w_router, router_bias, logits, T, H, E, ntiles, s);
-            else if (tg * ((ntiles + 3) / 4) >= 256)
-                rc = launch_route_wide<4, 4>(x, w_router, router_bias, logits, T, H, E, ntiles, s);
-            else if (tg * ((ntiles + 1) / 2) <= 256)
-                rc = launch_route_wide<2, 6>(x, w_router, router_bias, logits, T, H, E, ntiles, s);
-            else
-                rc = launch_route_wide<2, 3>(x, w_router, router_bias, logits, T, H, E, ntiles, s);
-            if (rc) return rc;
-        } else if (T <= 256 || ntiles < 8) {
-            // one batch of loads per slice at H = 2048 (16 k-steps)
-            hipLaunchKernelGGL((router_logits_kernel<1, 16>), dim3((unsigned)tblocks, (unsigned)ntiles),
-                               dim3(kRouteSlices * kWave), 0, s, (const uint16_t*)x, (const uint16_t*)w_router,
-                               router_bias, logits, T, (int)H, (int)E);
-        } else {
-            hipLaunchKernelGGL((router_logits_kernel<8, 8>), dim3((unsigned)tblocks, (unsigned)((ntiles + 7) / 8)),
-                               dim3(kRouteSlices * kWave), 0, s, (const uint16_t*)x, (const uint16_t*)w_router,
-                               router_bias, logits, T, (int)H, (int)E);
-        }
-        int rc = check_launch("moe_route (logits)");
-        if (rc) return rc;
-    }
+    return check_launch("moe_route (logits)");
+}
+
+static int route_topk(const float* logits, int32_t* topk_ids, float* topk_weights, int64_t T, int32_t E, int32_t k,
+                      int32_t norm_topk_prob, hipStream_t s) {
     const int64_t blocks = (T + kTopkWaves - 1) / kTopkWaves;
     if (blocks >= ((int64_t)1 << 31)) return set_error(MOE_ERR_UNSUPPORTED, "moe_route: T too large");
     if (k <= 16) {
@@ -487,4 +655,82 @@ extern "C" int moe_route(const void* x, const void* w_router, const float* route
     hipLaunchKernelGGL(route_topk_kernel, dim3((unsigned)blocks), dim3(kTopkWaves * kWave), 0, s, logits, topk_ids,
                        topk_weights, T, (int)E, (int)k, (int)(norm_topk_prob != 0));
     return check_launch("moe_route (top-k)");
+}
+
+// Checks of the (x, w_router, ..., k) arguments shared by both entry points.
+static int check_route_args(const char* fn, const void* x, const void* w_router, const float* logits,
+                            const int32_t* topk_ids, const float* topk_weights, int64_t T, int32_t H, int32_t E,
+                            int32_t k) {
+    if (x == nullptr) {
+        // logits are an input; H is not used
+        if (T < 0 || E < 0 || k < 0) return set_error(MOE_ERR_INVALID, "%s: negative size", fn);
+        if (E < 1 || E > kMaxExperts) return set_error(MOE_ERR_UNSUPPORTED, "%s: E=%d outside [1, 256]", fn, E);
+        if (k < 1 || k > E || k > kMaxTopK) return set_error(MOE_ERR_UNSUPPORTED, "%s: k=%d invalid", fn, k);
+        if (T * (int64_t)k >= ((int64_t)1 << 31)) return set_error(MOE_ERR_UNSUPPORTED, "%s: T*k too large", fn);
+    } else {
+        int rc = check_shape(fn, T, H, E, k, -1);
+        if (rc) return rc;
+        if (!w_router) return set_error(MOE_ERR_INVALID, "%s: w_router is NULL", fn);
+    }
+    if (T == 0) return MOE_OK;
+    if (!logits || !topk_ids || !topk_weights)
+        return set_error(MOE_ERR_INVALID, "%s: logits/topk_ids/topk_weights must not be NULL", fn);
+    if (x && (((uintptr_t)x | (uintptr_t)w_router) & 15))
+        return set_error(MOE_ERR_INVALID, "%s: x and w_router must be 16-byte aligned", fn);
+    return MOE_OK;
+}
+
+}  // namespace moe
+
+extern "C" int moe_route(const void* x, const void* w_router, const float* router_bias, float* logits,
+                         int32_t* topk_ids, float* topk_weights, int64_t T, int32_t H, int32_t E, int32_t k,
+                         int32_t norm_topk_prob, void* stream) {
+    using namespace moe;
+    clear_error();
+    int rc = check_route_args("moe_route", x, w_router, logits, topk_ids, topk_weights, T, H, E, k);
+    if (rc || T == 0) return rc;
+    hipStream_t s = (hipStream_t)stream;
+    if (x) {
+        rc = route_logits<false>(x, w_router, router_bias, logits, T, H, E, NormArgs{}, s);
+        if (rc) return rc;
+    }
+    return route_topk(logits, topk_ids, topk_weights, T, E, k, norm_topk_prob, s);
+}
+
+extern "C" int moe_fused_add_rmsnorm_route(const void* x, const void* residual, const void* norm_weight, float eps,
+                                           int32_t has_residual, void* x_out, void* residual_out,
+                                           const void* w_router, const float* router_bias, float* logits,
+                                           int32_t* topk_ids, float* topk_weights, int64_t T, int32_t H, int32_t E,
+                                           int32_t k, int32_t norm_topk_prob, void* stream) {
+    using namespace moe;
+    clear_error();
+    const char* fn = "moe_fused_add_rmsnorm_route";
+    if (!x) return set_error(MOE_ERR_INVALID, "%s: x is NULL", fn);
+    int rc = check_route_args(fn, x, w_router, logits, topk_ids, topk_weights, T, H, E, k);
+    if (rc) return rc;
+    if (H > 16384) return set_error(MOE_ERR_UNSUPPORTED, "%s: H=%d above 16384", fn, H);
+    if (!(eps >= 0.f)) return set_error(MOE_ERR_INVALID, "%s: eps must be >= 0", fn);
+    if (T == 0) return MOE_OK;
+    if (!norm_weight || !x_out || !residual_out || (has_residual && !residual))
+        return set_error(MOE_ERR_INVALID, "%s: required pointer is NULL", fn);
+    if (((uintptr_t)norm_weight | (uintptr_t)x_out | (uintptr_t)residual_out |
+         (uintptr_t)(has_residual ? residual : nullptr)) & 15)
+        return set_error(MOE_ERR_INVALID, "%s: pointers must be 16-byte aligned", fn);
+    // every router workgroup of a token block reads the block's rows while
+    // the first expert tile writes the outputs: they must be other memory
+    const char* in_lo[2] = {(const char*)x, (const char*)(has_residual ? residual : x)};
+    const char* out_lo[2] = {(const char*)x_out, (const char*)residual_out};
+    const size_t bytes = (size_t)T * H * 2;
+    for (const char* o : out_lo)
+        for (const char* i : in_lo)
+            if (o < i + bytes && i < o + bytes)
+                return set_error(MOE_ERR_INVALID, "%s: x_out and residual_out must not overlap x or residual", fn);
+    if (out_lo[0] < out_lo[1] + bytes && out_lo[1] < out_lo[0] + bytes)
+        return set_error(MOE_ERR_INVALID, "%s: x_out and residual_out must not overlap", fn);
+    hipStream_t s = (hipStream_t)stream;
+    const NormArgs na{(const uint16_t*)residual, (const uint16_t*)norm_weight, (uint16_t*)x_out,
+                      (uint16_t*)residual_out, eps, has_residual ? 1 : 0};
+    rc = route_logits<true>(x, w_router, router_bias, logits, T, H, E, na, s);
+    if (rc) return rc;
+    return route_topk(logits, topk_ids, topk_weights, T, E, k, norm_topk_prob, s);
 }

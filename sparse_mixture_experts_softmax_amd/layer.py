@@ -72,6 +72,7 @@ class MoEBuffers:
     out: torch.Tensor
     block_m: int
     cap: int
+    counters: Optional[torch.Tensor] = None  # zeroed arrival counters of the fused down + combine
 
 
 def allocate(T: int, H: int, E: int, k: int, I: int, device, block_m: Optional[int] = None,
@@ -99,6 +100,7 @@ def allocate(T: int, H: int, E: int, k: int, I: int, device, block_m: Optional[i
         out=torch.empty((T, H), dtype=out_dtype, device=device),
         block_m=block_m,
         cap=cap,
+        counters=torch.zeros((max(0, _lib.moe_combine_counter_count(T, H)),), dtype=torch.int32, device=device),
     )
 
 
@@ -121,6 +123,8 @@ def check_buffers(b: MoEBuffers, T: int, H: int, E: int, k: int, I: int, device)
             raise ValueError(f"buffers.{name} has shape {tuple(t.shape)}, the call needs {shape}")
         if t.device != torch.device(device):
             raise ValueError(f"buffers.{name} is on {t.device}, x on {device}")
+    if b.counters is not None and b.counters.numel() < _lib.moe_combine_counter_count(T, H):
+        raise ValueError("buffers.counters is too small for this call")
     ws = _lib.moe_align_workspace_bytes(T, k, E, b.block_m)
     have = 0 if b.workspace is None else b.workspace.numel() * b.workspace.element_size()
     if have < ws:
@@ -131,8 +135,12 @@ def moe_layer(x: torch.Tensor, w_router: torch.Tensor, w13: Optional[torch.Tenso
               w2: Optional[torch.Tensor] = None, *, top_k: int, norm_topk_prob: bool = True,
               router_bias: Optional[torch.Tensor] = None, packed: Optional[PackedExperts] = None,
               block_m: Optional[int] = None, out_dtype=torch.bfloat16, y_dtype=torch.float16,
-              buffers: Optional[MoEBuffers] = None, stream=None) -> torch.Tensor:
+              buffers: Optional[MoEBuffers] = None, fused_combine: bool = False, stream=None) -> torch.Tensor:
     """out[T, H] = sparse MoE layer of x[T, H] (no residual).
+
+    ``fused_combine``: run the down projection and the weighted combine as
+    one launch (moe_grouped_gemm_down_combine; same output bits) instead of
+    moe_grouped_gemm_down followed by moe_combine.
 
     x [T, H], w_router [E, H]: bf16 on the GPU; router_bias [E] fp32 or None.
     Expert weights either as ``packed`` (from pack_experts, the fast path)
@@ -172,10 +180,50 @@ def moe_layer(x: torch.Tensor, w_router: torch.Tensor, w13: Optional[torch.Tenso
                              b.num_padded, b.workspace, s)
     _lib.moe_grouped_gemm_gate_up_silu(x, w13p, b.sorted_ids, b.block_expert, b.num_padded, T, k, H, I, E, b.block_m,
                                        b.cap, b.act, s)
-    _lib.moe_grouped_gemm_down(b.act, w2p, b.sorted_ids, b.block_expert, b.num_padded, T, k, H, I, E, b.block_m, b.cap,
-                               b.y, s)
-    _lib.moe_combine(b.y, b.topk_weights, T, k, H, b.out, s)
+    if fused_combine:
+        _lib.moe_grouped_gemm_down_combine(b.act, w2p, b.sorted_ids, b.block_expert, b.num_padded, b.topk_weights, T, k,
+                                           H, I, E, b.block_m, b.cap, b.y, b.counters, b.out, s)
+    else:
+        _lib.moe_grouped_gemm_down(b.act, w2p, b.sorted_ids, b.block_expert, b.num_padded, T, k, H, I, E, b.block_m,
+                                   b.cap, b.y, s)
+        _lib.moe_combine(b.y, b.topk_weights, T, k, H, b.out, s)
     return b.out
+
+
+def moe_layer_with_norm(x: torch.Tensor, residual: Optional[torch.Tensor], norm_weight: torch.Tensor,
+                        w_router: torch.Tensor, *, top_k: int, packed: PackedExperts, eps: float = 1e-6,
+                        norm_topk_prob: bool = True, router_bias: Optional[torch.Tensor] = None,
+                        block_m: Optional[int] = None, out_dtype=torch.bfloat16, y_dtype=torch.float16,
+                        buffers: Optional[MoEBuffers] = None, stream=None):
+    """The decoder's post-attention residual add + RMSNorm and the MoE layer:
+    ``residual' = residual + x`` (``x`` when ``residual`` is None, the first
+    layer), ``h = rmsnorm(residual') * norm_weight``, ``out = moe(h)``. The
+    add and norm run inside the router kernel (moe_fused_add_rmsnorm_route);
+    the grouped GEMMs read ``h``. Returns (out, residual', h)."""
+    if x.dim() != 2:
+        raise ValueError("x [T,H] expected")
+    T, H = x.shape
+    E = w_router.shape[0]
+    I = packed.intermediate_size
+    k = int(top_k)
+    if buffers is not None:
+        check_buffers(buffers, T, H, E, k, I, x.device)
+        b = buffers
+    else:
+        b = allocate(T, H, E, k, I, x.device, block_m, out_dtype, y_dtype)
+    h = torch.empty_like(x)
+    res_out = torch.empty_like(x)
+    s = _lib._stream(stream, x)
+    _lib.moe_fused_add_rmsnorm_route(x, residual, norm_weight, eps, residual is not None, h, res_out, w_router,
+                                     router_bias, b.logits, b.topk_ids, b.topk_weights, T, H, E, k, norm_topk_prob, s)
+    _lib.moe_align_by_expert(b.topk_ids, T, k, E, b.block_m, b.sorted_ids, b.block_expert, b.expert_counts,
+                             b.num_padded, b.workspace, s)
+    _lib.moe_grouped_gemm_gate_up_silu(h, packed.w13, b.sorted_ids, b.block_expert, b.num_padded, T, k, H, I, E,
+                                       b.block_m, b.cap, b.act, s)
+    _lib.moe_grouped_gemm_down(b.act, packed.w2, b.sorted_ids, b.block_expert, b.num_padded, T, k, H, I, E,
+                               b.block_m, b.cap, b.y, s)
+    _lib.moe_combine(b.y, b.topk_weights, T, k, H, b.out, s)
+    return b.out, res_out, h
 
 
 def gated_mlp(x: torch.Tensor, packed: PackedExperts, *, block_m: Optional[int] = None, out_dtype=torch.bfloat16,
