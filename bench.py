@@ -141,8 +141,8 @@ def kernel_label(kind: str, block_m: int) -> str:
                 256: "grouped_gemm_wide_kernel<WideCfg<true,128,4,4,2,128>,false,false,2>"}[block_m]
     return {16: "grouped_gemm_skinny_kernel<false,4,4,4,true>", 32: "grouped_gemm_kernel<GemmCfg<32,128,false>,true>",
             64: "grouped_gemm_wide_kernel<WideCfg<false,64,4,4,2,128>,true,true,1>",
-            128: "grouped_gemm_wide_kernel<WideCfg<false,128,3,4,2,128>,true,true,1>",
-            256: "grouped_gemm_wide_kernel<WideCfg<false,128,3,4,2,128>,true,true,2>"}[block_m]
+            128: "grouped_gemm_wide_kernel<WideCfg<false,128,4,4,2,128>,true,true,1>",
+            256: "grouped_gemm_wide_kernel<WideCfg<false,128,4,4,2,128>,true,true,2>"}[block_m]
 
 
 def host_cpu_model() -> str:

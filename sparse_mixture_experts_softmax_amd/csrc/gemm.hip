@@ -364,8 +364,8 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(
 // with (BM/64) x 4 waves, two waves per SIMD.
 //
 // Operands reach LDS by direct global->LDS copies (global_load_lds_dwordx4,
-// no registers), S stages deep (128-row blocks: 4 for gate/up, all 160 KB of
-// LDS; 3 for down, where a fourth stage measured no faster): stage kt holds
+// no registers), S stages deep (128-row blocks: 4 stages of 40 KB, all of
+// LDS): stage kt holds
 // the activation rows' columns [32kt, 32kt+32) and one packed 1 KB block per
 // weight band. The A rows are stored 64 bytes apart with their four 16-byte
 // chunks XOR-swizzled by (row/4)%4 so that fragment reads are free of bank
@@ -955,11 +955,15 @@ static int dispatch_gemm(int32_t block_m, const void* a, const void* w, const in
             return launch_wide<WideCfg<GATED, 64, 4>, Y16, 1, OUTF>(a, w, sorted_ids, block_expert, num_padded, k,
                                                                     n_pairs, K, N_out, cap, out, s, what, ca);
         case 128:
-            return launch_wide<WideCfg<GATED, 128, GATED ? 4 : 3>, Y16, 1, OUTF>(
-                a, w, sorted_ids, block_expert, num_padded, k, n_pairs, K, N_out, cap, out, s, what, ca);
+            // 4 stages for both projections (down: -1 to -2.5% against 3 in
+            // same-box A/B runs on prefill, skewed and large); 3 stages for
+            // gate/up were 6% faster at prefill but need 32 bytes/lane of
+            // scratch, which this library does not allow
+            return launch_wide<WideCfg<GATED, 128, 4>, Y16, 1, OUTF>(a, w, sorted_ids, block_expert, num_padded, k,
+                                                                     n_pairs, K, N_out, cap, out, s, what, ca);
         case 256:  // two 128-row tiles per grouping block: the same bits as block_m 128 for every row
-            return launch_wide<WideCfg<GATED, 128, GATED ? 4 : 3>, Y16, 2, OUTF>(
-                a, w, sorted_ids, block_expert, num_padded, k, n_pairs, K, N_out, cap, out, s, what, ca);
+            return launch_wide<WideCfg<GATED, 128, 4>, Y16, 2, OUTF>(a, w, sorted_ids, block_expert, num_padded, k,
+                                                                     n_pairs, K, N_out, cap, out, s, what, ca);
     }
     return set_error(MOE_ERR_UNSUPPORTED, "%s: block_m=%d not in {16,32,64,128,256}", what, block_m);
 }
