@@ -86,7 +86,11 @@ __device__ __forceinline__ float row_total(float ss) {
     return ss;
 }
 
-template <int NTW, int U, bool NORM>
+// NORM: 0 = plain router; 1 = fused norm re-reading x and the residual in
+// the second pass; 2 = fused norm keeping the new residual rows in LDS
+// between the passes (16 x (H + 8) bf16, plus the norm weight: dynamic LDS)
+// and fetching the first batch of router fragments during the first pass.
+template <int NTW, int U, int NORM>
 __global__ __launch_bounds__(kRouteSlices* kWave) void router_logits_kernel(const uint16_t* __restrict__ x,
                                                                             const uint16_t* __restrict__ wr,
                                                                             const float* __restrict__ bias,
@@ -97,6 +101,7 @@ __global__ __launch_bounds__(kRouteSlices* kWave) void router_logits_kernel(cons
     constexpr int COLS = 16 * NTW;
     __shared__ float part[kRouteSlices][kRouteTokens][COLS + 1];
     __shared__ float part_ss[kRouteSlices][kRouteTokens];
+    extern __shared__ __attribute__((aligned(16))) char norm_lds[];
     const int lane = threadIdx.x % kWave, slice = threadIdx.x / kWave;
     const int64_t t0 = (int64_t)blockIdx.x * kRouteTokens;
     const int e0 = blockIdx.y * COLS;
@@ -119,27 +124,44 @@ __global__ __launch_bounds__(kRouteSlices* kWave) void router_logits_kernel(cons
     float inv = 0.f;
     const uint16_t* rrow = nullptr;
     const bool writer = NORM && blockIdx.y == 0 && row_ok;
-    if constexpr (NORM) {
+    const int rstride = H + 8;  // LDS row stride of the staged residual (16-byte pad against bank conflicts)
+    uint16_t* r_lds = (uint16_t*)norm_lds;
+    uint16_t* w_lds = r_lds + kRouteTokens * rstride;
+    u32x4 b0[U][NTW];  // NORM == 2: the first batch of router fragments, fetched during pass 1
+    if constexpr (NORM == 2) {
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int n = 0; n < NTW; ++n) b0[u][n] = ld16(wrow[n] + min(s_lo + u, ksteps - 1) * 32);
+        for (int h = (int)threadIdx.x * 8; h < H; h += kRouteSlices * kWave * 8) *(u32x4*)(w_lds + h) = ld16(na.w + h);
+    }
+    if constexpr (NORM != 0) {
         // pass 1: the row's sum of squares of the new residual (this wave's
         // slice, k-step by k-step, then the four lanes of a row, then the
         // four slices in order)
         rrow = na.has_res ? na.res + xoff : xrow;
+        constexpr int U1 = NORM == 2 ? 8 : U;
         float ss = 0.f;
+        auto take = [&](u32x4 xv, u32x4 rv, int s_) {
+            const u32x4 r = new_residual(xv, rv, na.has_res);
+            if constexpr (NORM == 2) *(u32x4*)(r_lds + row * rstride + s_ * 32 + koff) = r;
+            ss = add_squares(ss, r);
+        };
         int s = s_lo;
-        for (; s + U <= s_hi; s += U) {
-            u32x4 xv[U], rv[U];
+        for (; s + U1 <= s_hi; s += U1) {
+            u32x4 xv[U1], rv[U1];
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
+            for (int u = 0; u < U1; ++u) {
                 xv[u] = ld16(xrow + (s + u) * 32);
                 rv[u] = ld16(rrow + (s + u) * 32);
             }
 #pragma unroll
-            for (int u = 0; u < U; ++u) ss = add_squares(ss, new_residual(xv[u], rv[u], na.has_res));
+            for (int u = 0; u < U1; ++u) take(xv[u], rv[u], s + u);
         }
-        for (; s < s_hi; ++s) ss = add_squares(ss, new_residual(ld16(xrow + s * 32), ld16(rrow + s * 32), na.has_res));
+        for (; s < s_hi; ++s) take(ld16(xrow + s * 32), ld16(rrow + s * 32), s);
         ss = row_total(ss);
         if (lane < 16) part_ss[slice][row] = ss;
-        __syncthreads();
+        __syncthreads();  // also publishes the staged residual rows and norm weight
         float tot = 0.f;
 #pragma unroll
         for (int sl = 0; sl < kRouteSlices; ++sl) tot += part_ss[sl][row];
@@ -148,11 +170,12 @@ __global__ __launch_bounds__(kRouteSlices* kWave) void router_logits_kernel(cons
     // A operand of k-step s: the x chunk, or (fused norm) its normalized
     // value, written out with the new residual by the first expert tile
     auto a_chunk = [&](u32x4 xv, u32x4 rv, u32x4 wv, int s_) -> u32x4 {
-        if constexpr (!NORM) {
+        if constexpr (NORM == 0) {
             return sel(row_ok, xv);
         } else {
-            const u32x4 r = new_residual(xv, rv, na.has_res);
-            const u32x4 xn = normalized(r, wv, inv);
+            const u32x4 r = NORM == 2 ? *(const u32x4*)(r_lds + row * rstride + s_ * 32 + koff)
+                                      : new_residual(xv, rv, na.has_res);
+            const u32x4 xn = normalized(r, NORM == 2 ? *(const u32x4*)(w_lds + s_ * 32 + koff) : wv, inv);
             if (writer) {
                 *(u32x4*)(na.res_out + xoff + s_ * 32) = r;
                 *(u32x4*)(na.x_out + xoff + s_ * 32) = xn;
@@ -160,31 +183,58 @@ __global__ __launch_bounds__(kRouteSlices* kWave) void router_logits_kernel(cons
             return sel(row_ok, xn);
         }
     };
-    int s = s_lo;
-    for (; s + U <= s_hi; s += U) {
-        u32x4 a[U], b[U][NTW], rv[U], wv[U];
+    if constexpr (NORM == 2) {
+        // pass 2 from LDS: only the router fragments come from memory, the
+        // first batch already in flight
+        for (int s = s_lo; s < s_hi; s += U) {
+            u32x4 b[U][NTW];
+            if (s == s_lo) {
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            a[u] = ld16(xrow + (s + u) * 32);
-            if constexpr (NORM) {
-                rv[u] = ld16(rrow + (s + u) * 32);
-                wv[u] = ld16(na.w + (s + u) * 32 + koff);
+                for (int u = 0; u < U; ++u)
+#pragma unroll
+                    for (int n = 0; n < NTW; ++n) b[u][n] = b0[u][n];
+            } else {
+#pragma unroll
+                for (int u = 0; u < U; ++u)
+#pragma unroll
+                    for (int n = 0; n < NTW; ++n) b[u][n] = ld16(wrow[n] + min(s + u, ksteps - 1) * 32);
             }
 #pragma unroll
-            for (int n = 0; n < NTW; ++n) b[u][n] = ld16(wrow[n] + (s + u) * 32);
+            for (int u = 0; u < U; ++u) {
+                if (s + u >= s_hi) break;
+                const u32x4 zero{0u, 0u, 0u, 0u};
+                const u32x4 au = a_chunk(zero, zero, zero, s + u);
+#pragma unroll
+                for (int n = 0; n < NTW; ++n) acc[n] = mfma16x16x32(au, b[u][n], acc[n]);
+            }
         }
+    } else {
+        int s = s_lo;
+        for (; s + U <= s_hi; s += U) {
+            u32x4 a[U], b[U][NTW], rv[U], wv[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const u32x4 au = a_chunk(a[u], NORM ? rv[u] : a[u], NORM ? wv[u] : a[u], s + u);
+            for (int u = 0; u < U; ++u) {
+                a[u] = ld16(xrow + (s + u) * 32);
+                if constexpr (NORM == 1) {
+                    rv[u] = ld16(rrow + (s + u) * 32);
+                    wv[u] = ld16(na.w + (s + u) * 32 + koff);
+                }
 #pragma unroll
-            for (int n = 0; n < NTW; ++n) acc[n] = mfma16x16x32(au, b[u][n], acc[n]);
+                for (int n = 0; n < NTW; ++n) b[u][n] = ld16(wrow[n] + (s + u) * 32);
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const u32x4 au = a_chunk(a[u], NORM ? rv[u] : a[u], NORM ? wv[u] : a[u], s + u);
+#pragma unroll
+                for (int n = 0; n < NTW; ++n) acc[n] = mfma16x16x32(au, b[u][n], acc[n]);
+            }
         }
-    }
-    for (; s < s_hi; ++s) {
-        const u32x4 xv = ld16(xrow + s * 32);
-        const u32x4 a = a_chunk(xv, NORM ? ld16(rrow + s * 32) : xv, NORM ? ld16(na.w + s * 32 + koff) : xv, s);
+        for (; s < s_hi; ++s) {
+            const u32x4 xv = ld16(xrow + s * 32);
+            const u32x4 a = a_chunk(xv, NORM ? ld16(rrow + s * 32) : xv, NORM ? ld16(na.w + s * 32 + koff) : xv, s);
 #pragma unroll
-        for (int n = 0; n < NTW; ++n) acc[n] = mfma16x16x32(a, ld16(wrow[n] + s * 32), acc[n]);
+            for (int n = 0; n < NTW; ++n) acc[n] = mfma16x16x32(a, ld16(wrow[n] + s * 32), acc[n]);
+        }
     }
     // D layout: lane holds rows 4*(lane/16)+i, column lane%16 of each tile
 #pragma unroll
@@ -625,13 +675,28 @@ static int route_logits(const void* x, const void* w_router, const float* router
             rc = launch_route_wide<2, 3, NORM>(x, w_router, router_bias, logits, T, H, E, ntiles, na, s);
         if (rc) return rc;
     } else if (T <= 256 || ntiles < 8) {
-        // one batch of loads per slice at H = 2048 (16 k-steps; 8 with the
-        // fused norm, which also holds the residual and norm weight chunks)
-        hipLaunchKernelGGL((router_logits_kernel<1, NORM ? 8 : 16, NORM>), dim3((unsigned)tblocks, (unsigned)ntiles),
-                           dim3(kRouteSlices * kWave), 0, s, (const uint16_t*)x, (const uint16_t*)w_router,
-                           router_bias, logits, T, (int)H, (int)E, na);
+        // one batch of loads per slice at H = 2048 (16 k-steps). With the
+        // fused norm and H <= 4096 the new residual rows stay in LDS between
+        // the passes; above, the second pass re-reads x and the residual
+        // (batches of 8, as it also holds their chunks and the norm weight's).
+        const dim3 grid((unsigned)tblocks, (unsigned)ntiles), block(kRouteSlices * kWave);
+        if (!NORM) {
+            hipLaunchKernelGGL((router_logits_kernel<1, 16, 0>), grid, block, 0, s, (const uint16_t*)x,
+                               (const uint16_t*)w_router, router_bias, logits, T, (int)H, (int)E, na);
+        } else if (H <= 4096) {
+            const int lds = (kRouteTokens * (H + 8) + H) * 2;
+            static std::atomic<uint64_t> lds_set{0};
+            const int rc = ensure_dynamic_lds((const void*)router_logits_kernel<1, 16, 2>, 160 * 1024 - 8192,
+                                              lds_set, "moe_route");
+            if (rc) return rc;
+            hipLaunchKernelGGL((router_logits_kernel<1, 16, 2>), grid, block, lds, s, (const uint16_t*)x,
+                               (const uint16_t*)w_router, router_bias, logits, T, (int)H, (int)E, na);
+        } else {
+            hipLaunchKernelGGL((router_logits_kernel<1, 8, 1>), grid, block, 0, s, (const uint16_t*)x,
+                               (const uint16_t*)w_router, router_bias, logits, T, (int)H, (int)E, na);
+        }
     } else {
-        hipLaunchKernelGGL((router_logits_kernel<8, NORM ? 4 : 8, NORM>),
+        hipLaunchKernelGGL((router_logits_kernel<8, NORM ? 4 : 8, NORM ? 1 : 0>),
                            dim3((unsigned)tblocks, (unsigned)((ntiles + 7) / 8)), dim3(kRouteSlices * kWave), 0, s,
                            (const uint16_t*)x, (const uint16_t*)w_router, router_bias, logits, T, (int)H, (int)E, na);
     }

@@ -77,10 +77,14 @@ def _fused_route(x, r, w, wr, T, H, E, k, has_res, bias=None):
 @pytest.mark.parametrize("T,H,E,k,has_res", [(64, 2048, 128, 8, True), (4096, 2048, 128, 8, True),
                                              (8192, 4096, 128, 8, True), (300, 512, 40, 4, False),
                                              (16384, 2048, 128, 8, True), (1000, 2048, 256, 8, False),
-                                             (37, 192, 8, 2, True)])
+                                             (37, 192, 8, 2, True), (256, 4096, 64, 4, True),
+                                             (48, 8192, 32, 4, True), (300, 2112, 128, 8, True)])
 def test_fused_norm_route_matches_oracle(T, H, E, k, has_res):
-    """Small batches take the 16-token router kernel, larger ones the 64-token
-    workgroup-shared one (ring depths 2 to 3 with the residual chunks)."""
+    """Small batches take the 16-token router kernel (the new residual kept
+    in LDS between the passes up to H = 4096, re-read above: the 8192 case),
+    larger ones the 64-token workgroup-shared one (ring depths 2 to 3 with
+    the residual chunks), and large batches whose H does not suit its chunks
+    the 8-expert-tile kernel (the 2112 case)."""
     log(f"fused norm + route T={T} H={H} E={E} k={k} residual={has_res}")
     x = synth.normal_bf16(T + H, 81, (T, H), 1.0)
     r = synth.normal_bf16(T + H, 82, (T, H), 2.0)
