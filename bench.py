@@ -620,7 +620,8 @@ def record_stats(directory: str, workload: str):
     shape = synth.CONFIGS[workload]
     lines = [f"# rocprofv3 kernel statistics: {WORKLOAD_TEXT[workload]} (T={shape.T}, H={shape.H}, E={shape.E}, "
              f"k={shape.k}, I={shape.I})", "",
-             "Whole bench run (20 warm-up and 3 x 50 timed steps, plus the one-time weight packing and copies), "
+             "Whole bench run (20 warm-up and 3 x 50 timed steps of the layer, 20 + 50 steps with the down "
+             "projection and the combine fused, plus the one-time weight packing and copies), "
              "from the repository root on one MI355X (`export TMPDIR=/tmp` first; DIR = the output directory):", "",
              "```", stats_command(workload), "```", "",
              "| kernel | calls | average (us) | min (us) | max (us) | share of GPU time |", "|---|---|---|---|---|---|"]
@@ -667,7 +668,7 @@ def record_counters(directory: str, workload: str):
              "GRBM_GUI_ACTIVE summing the 8 XCDs' busy cycles.", "",
              "| kernel | step | FETCH_SIZE (KiB) | WRITE_SIZE (KiB) | HBM bytes (scaled) | MFMA busy |",
              "|---|---|---|---|---|---|"]
-    for kind in ("gate_up", "down", "combine", "route", "align"):
+    for kind in ("gate_up", "down", "down_combine", "combine", "route", "align"):
         names = [n for n in fe if _kind_of(n) == kind]
         for n in names:
             fb = fe[n]["FETCH_SIZE"] * 1024 * f_fac
@@ -696,10 +697,15 @@ def record_counters(directory: str, workload: str):
 
 def _kind_of(kernel_name: str) -> str:
     """Which step a kernel of the library belongs to, from its name (the
-    GEMMs' first boolean template argument is true for gate/up)."""
+    GEMMs' first boolean template argument is true for gate/up; their last
+    one is nonzero when the weighted combine is fused into the down
+    projection, moe_grouped_gemm_down_combine)."""
     if "grouped_gemm" in kernel_name:
         m = re.search(r"(?:WideCfg<|skinny_kernel<|GemmCfg<\d+, \d+, )(true|false)", kernel_name)
-        return "gate_up" if m and m.group(1) == "true" else "down"
+        if m and m.group(1) == "true":
+            return "gate_up"
+        last = re.search(r",\s*(\d+)>\s*$", kernel_name)
+        return "down_combine" if last and last.group(1) != "0" else "down"
     for kind, pat in (("combine", "combine"), ("route", "router"), ("route", "topk"), ("align", "align")):
         if pat in kernel_name:
             return kind
