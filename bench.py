@@ -2,7 +2,7 @@
 """Throughput of the fused sparse MoE layer on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode]
-                    [--also prefill,skewed,large] [--cpu-seconds 12]
+                    [--also medium,prefill,skewed,large] [--cpu-seconds 12]
 
 A step is one pass of the whole layer (route, align, gate/up GEMM + SiLU*mul,
 down GEMM, combine: the five C-ABI calls) over one batch of synthetic
@@ -21,9 +21,10 @@ algorithmic bytes or flops per launch over that duration). A third, short
 region with events around every call gives the per-kernel breakdown.
 
 The headline workload (default: decode, HBM-bound) is the JSON line's
-``value``; the matrix-core-bound workloads named by ``--also`` (default
-prefill, skewed and large) are measured in the same process, the same way,
-and reported under ``workloads``. Counter figures (HBM bytes, MFMA busy)
+``value``; the workloads named by ``--also`` (default: the mid-batch layer,
+HBM-bound like decode, and the matrix-core-bound prefill, skewed and large
+layers) are measured in the same process, the same way, and reported under
+``workloads``. Counter figures (HBM bytes, MFMA busy)
 come from committed rocprofv3 runs (profiles/counters.json) and are reported
 only while the kernel's source is unchanged since they were taken. The CPU
 oracle is timed on a bounded sample of the headline workload on the host
@@ -61,6 +62,7 @@ WORKLOAD_TEXT = {
     "prefill": "prefill-shaped Qwen3-MoE layer",
     "skewed": "skewed-routing (Zipf 1.2) MoE layer",
     "large": "large MoE layer on one GPU",
+    "medium": "mid-batch Qwen3-MoE layer (512 tokens, 32 rows per expert)",
     "dense": "dense SwiGLU GatedMLP (Qwen3-0.6B MLP shape) through the grouped GEMMs",
     "add_rmsnorm": "fused residual add + RMSNorm before the layer (prefill-shaped hidden state)",
 }
@@ -358,7 +360,7 @@ def measure_layer(workload: str, steps: int, warmup: int, seed: int, weights: We
     if dense:
         work["layer"]["flops"] -= 2 * T * H * E  # no router
 
-    bound = "hbm" if workload in ("decode", "tiny") else "mfma"
+    bound = "hbm" if workload in ("decode", "tiny", "medium") else "mfma"
 
     def roofline(kind, kern_ms):
         s = kern_ms * 1e-3
@@ -718,7 +720,7 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="decode", choices=list(WORKLOAD_TEXT))
-    ap.add_argument("--also", default="prefill,skewed,large",
+    ap.add_argument("--also", default="medium,prefill,skewed,large",
                     help="further workloads measured in the same run and reported under 'workloads' "
                          "(comma-separated; 'none' for none)")
     ap.add_argument("--also-steps", type=int, default=100, help="timed steps of each of those workloads")

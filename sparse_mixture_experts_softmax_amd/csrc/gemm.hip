@@ -1060,14 +1060,18 @@ extern "C" int moe_grouped_gemm_down_combine(const void* act, const void* w2, co
 
 extern "C" int32_t moe_pick_block_m(int64_t T, int32_t k, int32_t E) {
     if (T < 0 || k < 1 || E < 1) return -1;
-    // 16: weight streaming (skinny kernel), up to 16 rows per expert on
-    // average (at 16 both kernels take the same time on the decode-shaped
-    // layer; at 20, 32-row blocks are 10% faster); 32: few rows per expert;
-    // 128: the matrix-core bound regime, where the 8-wave 128x512 tile (two
-    // waves per SIMD) beats 64-row blocks despite the extra padding (measured
-    // on the prefill, skewed and large workloads).
+    // Crossovers of the whole layer's step time between block sizes, measured
+    // at the Qwen3-30B-A3B shape (H 2048, I 768, E 128, k 8) with near-uniform
+    // routing, T from 64 to 4096 (rows per expert = T * k / E on average):
+    // 16 (weight streaming, skinny kernel) up to 16 rows per expert (248 vs
+    // 252 us at 16, 266 vs 262 at 17); 32 up to 22 (262 vs 275; at 23 the
+    // 32-row blocks of the busier experts overflow into a second block: 284
+    // vs 276); 64 up to 60 (278 vs 292; at 64: 317 vs 294), where the wide
+    // kernel streams each expert's weights once for its one or two blocks
+    // (32-row blocks at 48 rows per expert: 403 vs 283 us); 128 above.
     const double rows_per_expert = (double)T * k / E;
     if (rows_per_expert <= 16) return 16;
-    if (rows_per_expert <= 64) return 32;
+    if (rows_per_expert <= 22) return 32;
+    if (rows_per_expert <= 60) return 64;
     return 128;
 }

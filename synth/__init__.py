@@ -151,6 +151,9 @@ CONFIGS = {
     "prefill": MoEShape("prefill", 4096, 2048, 128, 8, 768),
     "skewed": MoEShape("skewed", 16384, 2048, 128, 8, 768, skewed=True),
     "large": MoEShape("large", 8192, 4096, 128, 8, 1536),
+    # Between the decode- and prefill-shaped layers of the same model: 512
+    # tokens, 32 (token, slot) rows per expert on average.
+    "medium": MoEShape("medium", 512, 2048, 128, 8, 768),
     # Dense SwiGLU MLP of the Qwen3-0.6B layer the op-layer page prints
     # (gate_up_proj (6144, 1024), down_proj (1024, 3072)): one expert, k = 1.
     "dense": MoEShape("dense", 4096, 1024, 1, 1, 3072),

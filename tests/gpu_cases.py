@@ -11,7 +11,7 @@ import torch
 import synth
 import sparse_mixture_experts_softmax_amd as moe
 
-CONFIG_NAMES = ["tiny", "decode", "prefill", "skewed", "large"]
+CONFIG_NAMES = ["tiny", "decode", "medium", "prefill", "skewed", "large"]
 
 
 def log(msg: str):

@@ -236,7 +236,7 @@ def rows_covering_every_block(sorted_ids, npad, bm, n_pairs, seed=0):
 
 
 @pytest.mark.parametrize("name,y_dtype", [("tiny", F16), ("tiny", F32), ("decode", F16), ("decode", F32),
-                                          ("prefill", F16), ("prefill", F32), ("skewed", F16), ("skewed", F32),
+                                          ("medium", F16), ("prefill", F16), ("prefill", F32), ("skewed", F16), ("skewed", F32),
                                           ("large", F16)])
 def test_gemms_and_combine_against_oracle_steps(name, y_dtype):
     log(f"steps {name} y {y_dtype}")
@@ -322,8 +322,8 @@ def bf16_half_ulp(ref: np.ndarray) -> np.ndarray:
     return np.exp2(np.floor(np.log2(a)) - 8)
 
 
-@pytest.mark.parametrize("name,y_dtype", [("tiny", F16), ("tiny", F32), ("decode", F16), ("prefill", F16),
-                                          ("skewed", F16), ("large", F16), ("large", F32)])
+@pytest.mark.parametrize("name,y_dtype", [("tiny", F16), ("tiny", F32), ("decode", F16), ("medium", F16),
+                                          ("prefill", F16), ("skewed", F16), ("large", F16), ("large", F32)])
 def test_layer_matches_oracle(name, y_dtype):
     """Every token of every workload (so every row block and column tile of
     both GEMMs) against the oracle.
@@ -474,7 +474,7 @@ def test_nan_poison_unused_experts_and_pad_rows():
     assert np.array_equal(to_bits(out2), to_bits(clean))
 
 
-@pytest.mark.parametrize("name", ["decode", "prefill", "skewed", "large"])
+@pytest.mark.parametrize("name", ["decode", "medium", "prefill", "skewed", "large"])
 def test_run_twice_bit_identical(name):
     inp = host_inputs(name)
     dev = device_inputs(inp, key=name)
