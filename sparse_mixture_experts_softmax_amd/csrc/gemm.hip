@@ -378,8 +378,10 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(
 // Tiles are ordered so each XCD (workgroups go to the 8 XCDs round robin)
 // takes a contiguous share of the real (row block, N tile) pairs, row-block
 // major: the row blocks of one expert run together on one XCD and share its
-// L2 for the weight tile. The epilogue stages the output tile in LDS and
-// stores whole rows.
+// L2 for the weight tile. For gate/up the weights are the MFMA's first
+// operand, so each lane's accumulators hold runs of four consecutive output
+// columns of one row and act is stored straight from the registers; the
+// down projection's y rows go through LDS (see its epilogue).
 template <bool GATED_, int BM_, int STAGES_, int WAVES_N_ = 4, int TM_ = 2, int WTN_ = 128>
 struct WideCfg {
     static constexpr bool GATED = GATED_;
@@ -403,9 +405,9 @@ struct WideCfg {
     static_assert((STAGES - 1) * COPIES_PER_WAVE < 64, "vmcnt range");
     static_assert(STAGES * STAGE_BYTES <= 160 * 1024, "LDS");
     static_assert(THREADS >= BM, "one row id per thread");
-    // the epilogue reuses the stages: 1 KB of row ids, then the bf16 act tile
-    // or a 32-row pass of the fp32 y tile
-    static_assert(1024 + (GATED ? BM * COLS * 2 : 32 * COLS * 4) <= STAGES * STAGE_BYTES, "epilogue staging");
+    // the down epilogue reuses the stages: 1 KB of row ids, then 32 rows of
+    // the fp32 y tile at a time
+    static_assert(GATED || 1024 + 32 * COLS * 4 <= STAGES * STAGE_BYTES, "epilogue staging");
 };
 
 // Quarter-width tiles of the down projection's 128-row blocks (128 output
@@ -433,7 +435,11 @@ __device__ __forceinline__ void wide_tile(const uint16_t* __restrict__ a_src, co
 
     const int32_t* ids_blk = sorted_ids + (int64_t)mb * BM;
     auto real_row = [&](int32_t id) { return id >= 0 && (int64_t)id < n_pairs; };
-    const int32_t my_id = tid < BM ? ids_blk[tid] : 0;  // row ids for the epilogue (C::THREADS >= BM)
+    const int32_t my_id = tid < BM ? ids_blk[tid] : 0;  // row ids for the down epilogue (C::THREADS >= BM)
+    const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
+    int32_t rid[C::TM];  // gate/up: the flat (token, slot) index of this lane's row in each row block
+#pragma unroll
+    for (int i = 0; i < C::TM; ++i) rid[i] = ids_blk[wm * (32 * C::TM) + i * 32 + lane % 32];
 
     // This wave's copies: index q over [A rows 16q.. | B band q - BM/16],
     // each a uniform base (the activations or this expert's weights) plus a
@@ -481,7 +487,6 @@ __device__ __forceinline__ void wide_tile(const uint16_t* __restrict__ a_src, co
         }
     };
 
-    const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
     // B band pairs (32 weight rows) of each accumulator column tile
     int band_lo[C::TN], band_hi[C::TN];
 #pragma unroll
@@ -535,7 +540,9 @@ __device__ __forceinline__ void wide_tile(const uint16_t* __restrict__ a_src, co
 #pragma unroll
             for (int i = 0; i < C::TM; ++i)
 #pragma unroll
-                for (int t = 0; t < C::TN; ++t) acc[i][t] = mfma32x32x16(fa[ks][i], fb[ks][t], acc[i][t]);
+                for (int t = 0; t < C::TN; ++t)
+                    acc[i][t] = C::GATED ? mfma32x32x16(fb[ks][t], fa[ks][i], acc[i][t])
+                                         : mfma32x32x16(fa[ks][i], fb[ks][t], acc[i][t]);
     };
 
     // Prologue: the first S-1 stages (when K has fewer k-steps, the extra
@@ -564,62 +571,51 @@ __device__ __forceinline__ void wide_tile(const uint16_t* __restrict__ a_src, co
         for (int kt = 0; kt < nkt; ++kt) kstep(kt, std::false_type{});
     }
 
-    // The stages are free once every wave is done with the last one: they
-    // now hold the block's row ids (first 1 KB) and the output tile, staged
-    // so that every global store writes whole rows, 16 bytes per lane (the
-    // accumulator layout gives each lane one column, so direct stores would
-    // write 2- or 4-byte pieces).
-    __syncthreads();
-    int32_t* ids_s = (int32_t*)smem;
-    char* stile = smem + 1024;
-    if (tid < BM) ids_s[tid] = my_id;
-    __syncthreads();
-
-    // Element q of a 32x32 accumulator tile is row 8*(q/4) + 4*(lane/32) +
-    // q%4, column lane%32; the ids of rows q..q+3 come as one 16-byte read.
-    if (C::GATED) {
-        // the whole BM x COLS bf16 tile at once, row-major with the 16-byte
-        // chunks of row r XOR-swizzled by r%16 (the packed read-out below
-        // gathers 16 rows at one column: without it they share a bank)
-        uint16_t* st = (uint16_t*)stile;
+    if constexpr (C::GATED) {
+        // Straight from the accumulators: with the weights as the MFMA's
+        // first operand, element q of accumulator tile (i, g) is output
+        // column 8*(q/4) + 4*(lane/32) + q%4 of 32-column block g and row
+        // lane%32 of 32-row block i, so for each q/4 a lane holds four
+        // consecutive columns of one row and lanes l and l+32 together 16
+        // contiguous bytes of it.
+        // act in fragment blocks (16 rows x 32 columns, 1 KB): the 8-column
+        // chunk q/4 of row R sits at chunk*16 + R%16 within its block, so
+        // each store instruction writes two runs of 256 contiguous bytes
 #pragma unroll
-        for (int g = 0; g < C::TN / 2; ++g) {
-            const int col = wn * (C::WTN / 2) + g * 32 + lane % 32;
+        for (int i = 0; i < C::TM; ++i) {
+            const int64_t R = (int64_t)mb * BM + wm * (32 * C::TM) + i * 32 + lane % 32;  // act row
+            const bool real = real_row(rid[i]);  // pad rows are written as zeros
 #pragma unroll
-            for (int i = 0; i < C::TM; ++i)
+            for (int g = 0; g < C::TN / 2; ++g) {
+                const int cb = col0 + wn * (C::WTN / 2) + g * 32;  // 32-column block (N_out % 32 == 0)
+                if (cb >= N_out) continue;
+                uint16_t* blk = (uint16_t*)out + ((R / 16) * (N_out / 32) + cb / 32) * 512 + (R % 16) * 8 +
+                                4 * (lane / 32);
 #pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4) {
-                    const int row0 = wm * (32 * C::TM) + i * 32 + 8 * q4 + 4 * (lane / 32);
-                    const int4 id4 = *(const int4*)&ids_s[row0];
-                    const int32_t ids[4] = {id4.x, id4.y, id4.z, id4.w};
+                for (int c8 = 0; c8 < 4; ++c8) {
+                    float v[4];
 #pragma unroll
                     for (int u = 0; u < 4; ++u) {
-                        const int q = 4 * q4 + u;
-                        const float v = silu(acc[i][g][q]) * acc[i][g + C::TN / 2][q];
-                        const int r = row0 + u;
-                        st[r * C::COLS + (((col >> 3) ^ (r & 15)) << 3) + (col & 7)] =
-                            f32_to_bf16(real_row(ids[u]) ? v : 0.f);
+                        const int q = 4 * c8 + u;
+                        v[u] = real ? silu(acc[i][g][q]) * acc[i][g + C::TN / 2][q] : 0.f;
                     }
+                    const u32x2 p = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+                    __builtin_nontemporal_store(p, (u32x2*)(blk + c8 * 128));
                 }
-        }
-        __syncthreads();
-        // act is stored as fragment blocks (16 rows x 32 columns, 1 KB):
-        // consecutive threads write consecutive 16-byte lanes of a block
-        constexpr int CPR = C::COLS * 2 / 16;  // 16-byte chunks per staged row
-        constexpr int KB = C::COLS / 32;       // column blocks per tile
-        static_assert(CPR >= 16, "the chunk swizzle needs 16 chunks per row");
-        for (int ci = tid; ci < (BM / 16) * KB * kWave; ci += C::THREADS) {
-            const int blk = ci / kWave, l = ci % kWave;
-            const int band = blk / KB, kb = blk % KB;
-            const int r = band * 16 + l % 16, chunk = kb * 4 + l / 16;
-            const int col = col0 + kb * 32;
-            const u32x4 v = *(const u32x4*)(stile + (r * CPR + (chunk ^ (r & 15))) * 16);
-            if (col < N_out)
-                __builtin_nontemporal_store(
-                    v, (u32x4*)((uint16_t*)out + ((int64_t)(mb * (BM / 16) + band) * (N_out / 32) + col / 32) * 512 +
-                                l * 8));
+            }
         }
     } else {
+        // y rows are whole 1 KB (fp16) or 2 KB (fp32) runs of scattered rows,
+        // so they are staged: the stages are free once every wave is done
+        // with the last one, and hold the block's row ids (first 1 KB) and
+        // 32 rows of the tile at a time, each row then stored 16 bytes per
+        // lane (straight from the accumulators each lane would write 16-byte
+        // pieces of 32 rows: 2.8x slower at prefill)
+        __syncthreads();
+        int32_t* ids_s = (int32_t*)smem;
+        char* stile = smem + 1024;
+        if (tid < BM) ids_s[tid] = my_id;
+        __syncthreads();
         // 32-row passes (one accumulator tile row of the waves of one wm)
         constexpr int ES = Y16 ? 2 : 4;
         constexpr int CPR = C::COLS * ES / 16;  // 16-byte chunks per row

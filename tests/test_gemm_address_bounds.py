@@ -9,7 +9,9 @@ straddle the end of a row: the down projection with I % 64 == 32), of the
 skinny 16-row kernel and of the wide kernel's direct-to-LDS copies, from the
 same index formulas as the HIP source, over a routing produced by the CPU
 oracle's grouping, and check them against the buffer sizes the library
-documents (x: T*H, act: cap*I, packed weights: E*N*K elements)."""
+documents (x: T*H, act: cap*I, packed weights: E*N*K elements). The gate/up
+wide kernel's act stores, taken straight from the accumulators, are replayed
+the same way."""
 import numpy as np
 import pytest
 
@@ -221,3 +223,43 @@ def test_wide_kernel_copies_in_bounds_block_m_256():
     a, b = _wide_copies(False, 128, sorted_ids, block_expert, npad, T, k, I, H, E, am=2)
     _check(a, cap * I, "act")
     _check(b, E * H * I, "w2")
+
+
+
+def _wide_act_stores(bm, tm, waves_n, wtn, npad, N_out, col_tiles):
+    """Element offsets of act written by the gate/up wide kernel's epilogue
+    (straight from the accumulators: lane l holds row l%32 of each 32-row
+    block and four consecutive columns 8*c8 + 4*(l/32) .. +3 of each
+    32-column block), with the logical (row, column) of each."""
+    lane = np.arange(64)
+    waves_m = bm // (32 * tm)
+    offs, rows, cols = [], [], []
+    for mb in range(npad // bm):
+        for col0 in col_tiles:
+            for wm in range(waves_m):
+                for wn in range(waves_n):
+                    for i in range(tm):
+                        R = mb * bm + wm * 32 * tm + i * 32 + lane % 32
+                        for g in range(wtn // 64):
+                            cb = col0 + wn * (wtn // 2) + g * 32
+                            if cb >= N_out:
+                                continue
+                            for c8 in range(4):
+                                for u in range(4):
+                                    offs.append(((R // 16) * (N_out // 32) + cb // 32) * 512 + (R % 16) * 8 +
+                                                4 * (lane // 32) + c8 * 128 + u)
+                                    rows.append(R)
+                                    cols.append(cb + 8 * c8 + 4 * (lane // 32) + u)
+    return np.concatenate(offs), np.concatenate(rows), np.concatenate(cols)
+
+
+@pytest.mark.parametrize("bm", [64, 128])
+@pytest.mark.parametrize("T,H,E,k,I", [(700, 192, 8, 2, 160), (520, 128, 4, 1, 96), (300, 256, 16, 4, 288)])
+def test_wide_kernel_act_stores_cover_rows_once(bm, T, H, E, k, I):
+    """The act stores of gate/up write every element of rows [0, num_padded)
+    exactly once (pad rows as zeros), each at its fragment-layout offset."""
+    _, _, npad = _routing(T, k, E, bm, T + bm + I)
+    # 8 waves as (bm/64) x 4 with 64x128 wave tiles, 256 output columns per tile
+    offs, rows, cols = _wide_act_stores(bm, 2, 4, 128, npad, I, range(0, I, 256))
+    assert np.array_equal(offs, _frag_index(rows, cols, I)), "act offsets follow the fragment layout"
+    assert np.array_equal(np.sort(offs), np.arange(npad * I)), "every act element of the real blocks once"
