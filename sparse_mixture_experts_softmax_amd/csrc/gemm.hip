@@ -14,7 +14,8 @@
 // Three kernels, chosen by the row-block size block_m:
 //   16       grouped_gemm_skinny_kernel (weight streaming, decode-sized)
 //   32       grouped_gemm_kernel        (16x16x32 MFMA, LDS-staged)
-//   64, 128  grouped_gemm_wide_kernel   (32x32x16 MFMA, direct-to-LDS copies)
+//   64, 128  grouped_gemm_wide_kernel   (32x32x16 MFMA, direct-to-LDS copies;
+//   and 256  256-row blocks as two 128-row tiles)
 // The skinny and general kernels launch one workgroup per (row block, N
 // tile) of the capacity and blocks past num_padded (read on the device)
 // return at once; the wide kernel launches one persistent workgroup per CU
