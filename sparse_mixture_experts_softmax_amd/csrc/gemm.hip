@@ -573,15 +573,14 @@ __device__ __forceinline__ void wide_tile(const uint16_t* __restrict__ a_src, co
     }
 
     if constexpr (C::GATED) {
-        // Straight from the accumulators: with the weights as the MFMA's
-        // first operand, element q of accumulator tile (i, g) is output
-        // column 8*(q/4) + 4*(lane/32) + q%4 of 32-column block g and row
-        // lane%32 of 32-row block i, so for each q/4 a lane holds four
-        // consecutive columns of one row and lanes l and l+32 together 16
-        // contiguous bytes of it.
-        // act in fragment blocks (16 rows x 32 columns, 1 KB): the 8-column
-        // chunk q/4 of row R sits at chunk*16 + R%16 within its block, so
-        // each store instruction writes two runs of 256 contiguous bytes
+        // Straight from the accumulators, no LDS. With the weights as the
+        // MFMA's first operand, element q of accumulator tile (i, g) is
+        // output column 8*(q/4) + 4*(lane/32) + q%4 of 32-column block g and
+        // row lane%32 of 32-row block i: for each q/4 a lane holds four
+        // consecutive columns of one row, and lanes l and l+32 together one
+        // 8-column chunk. In act's fragment blocks (16 rows x 32 columns,
+        // 1 KB) chunk q/4 of row R sits at chunk*16 + R%16, so each store
+        // instruction writes two runs of 256 contiguous bytes.
 #pragma unroll
         for (int i = 0; i < C::TM; ++i) {
             const int64_t R = (int64_t)mb * BM + wm * (32 * C::TM) + i * 32 + lane % 32;  // act row
