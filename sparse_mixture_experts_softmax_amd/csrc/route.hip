@@ -321,25 +321,46 @@ __global__ __launch_bounds__(kRouteSlices* kWave) void router_logits_wide_kernel
     const uint16_t* xsrc = x + xoff;
     const uint16_t* rsrc = NORM ? (na.has_res ? na.res + xoff : xsrc) : nullptr;
     const bool writer = NORM && blockIdx.y == 0 && t0 + row < T;
+    // Copies of 8 rows x 2 k-steps (128 contiguous bytes of each row): copy
+    // lane l fetches piece (l%8) ^ (l/8) of row l/8 (a piece is 8 elements;
+    // pieces 0-3 are the first k-step), so piece p of row r lands in slot
+    // r*8 + (p ^ r), which keeps the fragment reads of 8 consecutive rows on
+    // distinct banks. Copy index: (16-row tile, 8-row half, k-step pair).
+    const int crow = lane / 8, cpiece = (lane % 8) ^ (lane / 8);
     const uint16_t* wsrc[C::W_COPIES];
-    int wdst[C::W_COPIES];
 #pragma unroll
     for (int j = 0; j < C::W_COPIES; ++j) {
-        const int f = wave * C::W_COPIES + j;  // fragment (expert tile f / RC, k-step f % RC)
-        wsrc[j] = wr + (int64_t)min(e0 + 16 * (f / RC) + row, E - 1) * H + (f % RC) * 32 + koff;
-        wdst[j] = f * 1024;
+        const int f = wave * C::W_COPIES + j;
+        const int pr = f % (RC / 2), half = (f / (RC / 2)) % 2, tile = f / RC;
+        wsrc[j] = wr + (int64_t)min(e0 + 16 * tile + 8 * half + crow, E - 1) * H + pr * 64 + cpiece * 8;
     }
+    const uint16_t* xcp[2];
+    const uint16_t* rcp[2];
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+        const int64_t off = min(t0 + 8 * half + crow, T - 1) * (int64_t)H + cpiece * 8;
+        xcp[half] = x + off;
+        rcp[half] = NORM ? (na.has_res ? na.res + off : x + off) : nullptr;
+    }
+    // slot of this lane's fragment (row lane%16, k offset koff) of k-step s
+    // within the copies of its 8-row half
+    auto frag_slot = [&](int s) { return ((lane % 8) * 8 + (((s % 2) * 4 + lane / 16) ^ (lane % 8))) * 16; };
     const int ksteps = H / 32, per = ksteps / kRouteSlices, nchunk = ksteps / RC;
     auto issue = [&](int c) {
         char* buf = smem + (c % NB) * C::CHUNK_BYTES;
 #pragma unroll
-        for (int j = 0; j < C::W_COPIES; ++j) lds_dma16(wsrc[j] + c * RC * 32, buf + wdst[j]);
+        for (int j = 0; j < C::W_COPIES; ++j) lds_dma16(wsrc[j] + c * RC * 32, buf + (wave * C::W_COPIES + j) * 1024);
 #pragma unroll
-        for (int s = 0; s < RC; ++s) lds_dma16(xsrc + (c * RC + s) * 32, buf + C::W_BYTES + (wave * RC + s) * 1024);
+        for (int q = 0; q < RC; ++q) {
+            const int pr = q % (RC / 2), half = q / (RC / 2);
+            lds_dma16(xcp[half] + c * RC * 32 + pr * 64, buf + C::W_BYTES + (wave * RC + q) * 1024);
+        }
         if constexpr (NORM) {
 #pragma unroll
-            for (int s = 0; s < RC; ++s)
-                lds_dma16(rsrc + (c * RC + s) * 32, buf + C::W_BYTES + C::X_BYTES + (wave * RC + s) * 1024);
+            for (int q = 0; q < RC; ++q) {
+                const int pr = q % (RC / 2), half = q / (RC / 2);
+                lds_dma16(rcp[half] + c * RC * 32 + pr * 64, buf + C::W_BYTES + C::X_BYTES + (wave * RC + q) * 1024);
+            }
         }
     };
     f32x4 acc[kRouteSlices][ET];
@@ -395,10 +416,13 @@ __global__ __launch_bounds__(kRouteSlices* kWave) void router_logits_wide_kernel
             const char* buf = smem + (c % NB) * C::CHUNK_BYTES;
 #pragma unroll
             for (int s = 0; s < RC; ++s) {
-                u32x4 a = *(const u32x4*)(buf + C::W_BYTES + (wave * RC + s) * 1024 + lane * 16);
+                // this lane's 8-row half and k-step pair
+                const int xq = (row / 8) * (RC / 2) + s / 2;
+                u32x4 a = *(const u32x4*)(buf + C::W_BYTES + (wave * RC + xq) * 1024 + frag_slot(s));
                 if constexpr (NORM) {
                     const int ks = c * RC + s;
-                    const u32x4 rv = *(const u32x4*)(buf + C::W_BYTES + C::X_BYTES + (wave * RC + s) * 1024 + lane * 16);
+                    const u32x4 rv =
+                        *(const u32x4*)(buf + C::W_BYTES + C::X_BYTES + (wave * RC + xq) * 1024 + frag_slot(s));
                     const u32x4 r = new_residual(a, rv, na.has_res);
                     a = normalized(r, *(const u32x4*)(w_lds + ks * 32 + koff), inv);
                     if (writer) {
@@ -408,7 +432,7 @@ __global__ __launch_bounds__(kRouteSlices* kWave) void router_logits_wide_kernel
                 }
 #pragma unroll
                 for (int j = 0; j < ET; ++j)
-                    acc[sl][j] = mfma16x16x32(a, *(const u32x4*)(buf + (j * RC + s) * 1024 + lane * 16), acc[sl][j]);
+                    acc[sl][j] = mfma16x16x32(a, *(const u32x4*)(buf + (j * RC + xq) * 1024 + frag_slot(s)), acc[sl][j]);
             }
         }
     }
