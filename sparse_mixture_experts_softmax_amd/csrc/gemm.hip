@@ -383,9 +383,10 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(
 // operand, so each lane's accumulators hold runs of four consecutive output
 // columns of one row and act is stored straight from the registers; the
 // down projection's y rows go through LDS (see its epilogue).
-template <bool GATED_, int BM_, int STAGES_, int WAVES_N_ = 4, int TM_ = 2, int WTN_ = 128>
+template <bool GATED_, int BM_, int STAGES_, int WAVES_N_ = 4, int TM_ = 2, int WTN_ = 128, int MINB_ = 1>
 struct WideCfg {
     static constexpr bool GATED = GATED_;
+    static constexpr int MINB = MINB_;           // workgroups per CU (LDS permitting)
     static constexpr int BM = BM_;
     static constexpr int TM = TM_;               // 32-row accumulator tiles per wave
     static constexpr int WAVES_N = WAVES_N_;
@@ -404,7 +405,7 @@ struct WideCfg {
     static_assert(COPIES % (WAVES_M * WAVES_N) == 0, "copies must split evenly over the waves");
     static_assert(STAGES >= 2 && STAGES <= 6, "stages");
     static_assert((STAGES - 1) * COPIES_PER_WAVE < 64, "vmcnt range");
-    static_assert(STAGES * STAGE_BYTES <= 160 * 1024, "LDS");
+    static_assert(MINB * STAGES * STAGE_BYTES <= 160 * 1024, "LDS");
     static_assert(THREADS >= BM, "one row id per thread");
     // the down epilogue reuses the stages: 1 KB of row ids, then 32 rows of
     // the fp32 y tile at a time
@@ -670,7 +671,7 @@ __device__ __forceinline__ void wide_tile(const uint16_t* __restrict__ a_src, co
 // each expert to 256 rows and every 256-row block is computed as two 128-row
 // tiles (AM = 2) of the same expert, so the row block of tile mb is mb / AM.
 template <class C, bool Y16, bool SPLIT, int AM = 1, int OUTF = 0>
-__global__ __launch_bounds__(C::THREADS) void grouped_gemm_wide_kernel(
+__global__ __launch_bounds__(C::THREADS, C::MINB* C::THREADS / 256) void grouped_gemm_wide_kernel(
     const uint16_t* __restrict__ a_src, const uint16_t* __restrict__ w, const int32_t* __restrict__ sorted_ids,
     const int32_t* __restrict__ block_expert, const int32_t* __restrict__ num_padded, int k, int64_t n_pairs,
     int K, int N_out, int n_tiles, void* __restrict__ out, CombineArgs ca) {
@@ -728,16 +729,17 @@ static int launch_wide(const void* a, const void* w, const int32_t* sorted_ids, 
                          "%s: block_m=%d needs the activations (%lld bytes) and one expert's weights (%lld bytes) "
                          "under 4 GiB; split the batch",
                          what, C::BM, (long long)a_bytes, (long long)w_bytes);
-    // one workgroup per compute unit at most (160 KB of LDS each), a multiple
-    // of 8 so that every XCD gets the same number
+    // C::MINB workgroups per compute unit at most (160 KB of LDS between
+    // them), a multiple of 8 so that every XCD gets the same number
     const int cus = device_cu_count(what);
     if (cus < 0) return cus;
     int64_t grid = (cap / C::BM) * n_tiles;
     grid = (grid + 7) / 8 * 8;
-    grid = min(grid, (int64_t)max(8, cus / 8 * 8));
+    grid = min(grid, (int64_t)max(8, cus / 8 * 8) * C::MINB);
     if (grid >= ((int64_t)1 << 31)) return set_error(MOE_ERR_UNSUPPORTED, "%s: grid too large", what);
     const size_t lds = (size_t)C::STAGES * C::STAGE_BYTES;
-    constexpr bool SPLIT = !C::GATED;  // quarter tiles for the down projection's last round
+    // quarter tiles for the down projection's last round (one workgroup per CU)
+    constexpr bool SPLIT = !C::GATED && C::MINB == 1;
     static std::atomic<uint64_t> lds_set{0};
     const int rc =
         ensure_dynamic_lds((const void*)grouped_gemm_wide_kernel<C, Y16, SPLIT, AM, OUTF>, (int)lds, lds_set, what);
@@ -948,8 +950,12 @@ static int dispatch_gemm(int32_t block_m, const void* a, const void* w, const in
             return launch_gemm<GemmCfg<32, 128, GATED>, Y16, OUTF>(a, w, sorted_ids, block_expert, num_padded, k,
                                                                    n_pairs, K, N_out, cap, out, s, what, ca);
         case 64:
-            return launch_wide<WideCfg<GATED, 64, 4>, Y16, 1, OUTF>(a, w, sorted_ids, block_expert, num_padded, k,
-                                                                    n_pairs, K, N_out, cap, out, s, what, ca);
+            // 64x256 tiles, four waves of 32x128, four 20 KB stages, two
+            // workgroups per CU: at 32 rows per expert (weight streaming)
+            // gate/up -9% and down -7% against 64x512 tiles with one
+            // workgroup per CU (same-process probe, outputs identical)
+            return launch_wide<WideCfg<GATED, 64, 4, 2, 1, 128, 2>, Y16, 1, OUTF>(
+                a, w, sorted_ids, block_expert, num_padded, k, n_pairs, K, N_out, cap, out, s, what, ca);
         case 128:
             // 4 stages for both projections (down: -1 to -2.5% against 3 in
             // same-box A/B runs on prefill, skewed and large); 3 stages for
@@ -1059,15 +1065,15 @@ extern "C" int32_t moe_pick_block_m(int64_t T, int32_t k, int32_t E) {
     // Crossovers of the whole layer's step time between block sizes, measured
     // at the Qwen3-30B-A3B shape (H 2048, I 768, E 128, k 8) with near-uniform
     // routing, T from 64 to 4096 (rows per expert = T * k / E on average):
-    // 16 (weight streaming, skinny kernel) up to 16 rows per expert (248 vs
-    // 252 us at 16, 266 vs 262 at 17); 32 up to 22 (262 vs 275; at 23 the
-    // 32-row blocks of the busier experts overflow into a second block: 284
-    // vs 276); 64 up to 60 (278 vs 292; at 64: 317 vs 294), where the wide
-    // kernel streams each expert's weights once for its one or two blocks
-    // (32-row blocks at 48 rows per expert: 403 vs 283 us); 128 above.
+    // 16 (weight streaming, skinny kernel) below 16 rows per expert (239 vs
+    // 242 us at 15; at 16 the busier experts need a second 16-row block: 248
+    // vs 242); 64 (64x256 tiles, two workgroups per CU) up to 60 (284 vs 285
+    // at 60, 278 vs 286 at 56; at 64 rows: 298 vs 287), where it streams each
+    // expert's weights once for its one or two blocks and beats the 32-row
+    // kernel at every size (257 vs 248 us at 20 rows, 349 vs 251 at 32); 128
+    // above.
     const double rows_per_expert = (double)T * k / E;
-    if (rows_per_expert <= 16) return 16;
-    if (rows_per_expert <= 22) return 32;
+    if (rows_per_expert < 16) return 16;
     if (rows_per_expert <= 60) return 64;
     return 128;
 }

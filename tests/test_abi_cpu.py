@@ -45,8 +45,8 @@ def test_capacity_and_workspace():
     assert moe.moe_align_workspace_bytes(128, 8, 128, 64) == 0  # one tile
     for T, k, E in ((64, 8, 128), (4096, 8, 128), (16, 2, 8)):
         assert moe.moe_pick_block_m(T, k, E) in (16, 32, 64, 128)
-    # the measured crossovers, in rows per expert (T * k / E): 16 | 22 | 60
-    picks = {256: 16, 272: 32, 352: 32, 368: 64, 512: 64, 960: 64, 976: 128, 4096: 128}
+    # the measured crossovers, in rows per expert (T * k / E): below 16 | up to 60
+    picks = {64: 16, 240: 16, 255: 16, 256: 64, 352: 64, 512: 64, 960: 64, 976: 128, 4096: 128}
     for T, bm in picks.items():
         assert moe.moe_pick_block_m(T, 8, 128) == bm, T
     assert moe.moe_pick_block_m(-1, 8, 128) == -1 and moe.moe_pick_block_m(4, 0, 8) == -1

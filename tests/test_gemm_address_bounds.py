@@ -202,10 +202,11 @@ def _wide_copies(gated, bm, sorted_ids, block_expert, npad, T, k, K, N_out, E, b
 def test_wide_kernel_copies_in_bounds(bm, T, H, E, k, I):
     sorted_ids, block_expert, npad = _routing(T, k, E, bm, T + bm)
     cap = len(sorted_ids)
-    a, b = _wide_copies(True, bm, sorted_ids, block_expert, npad, T, k, H, I, E)
+    bn = 256 if bm == 64 else 512  # weight rows per tile: 64x256 and 128x512 tiles
+    a, b = _wide_copies(True, bm, sorted_ids, block_expert, npad, T, k, H, I, E, bn=bn)
     _check(a, T * H, "x")
     _check(b, E * 2 * I * H, "w13")
-    a, b = _wide_copies(False, bm, sorted_ids, block_expert, npad, T, k, I, H, E)
+    a, b = _wide_copies(False, bm, sorted_ids, block_expert, npad, T, k, I, H, E, bn=bn)
     _check(a, cap * I, "act")
     _check(b, E * H * I, "w2")
     # quarter-width down tiles: 128 weight rows from band tn*32 + sub*8
@@ -259,7 +260,9 @@ def test_wide_kernel_act_stores_cover_rows_once(bm, T, H, E, k, I):
     """The act stores of gate/up write every element of rows [0, num_padded)
     exactly once (pad rows as zeros), each at its fragment-layout offset."""
     _, _, npad = _routing(T, k, E, bm, T + bm + I)
-    # 8 waves as (bm/64) x 4 with 64x128 wave tiles, 256 output columns per tile
-    offs, rows, cols = _wide_act_stores(bm, 2, 4, 128, npad, I, range(0, I, 256))
+    if bm == 128:  # 8 waves as 2 x 4 with 64x128 wave tiles, 256 output columns per tile
+        offs, rows, cols = _wide_act_stores(bm, 2, 4, 128, npad, I, range(0, I, 256))
+    else:  # 64x256 tiles: 4 waves as 2 x 2 with 32x128 wave tiles, 128 output columns
+        offs, rows, cols = _wide_act_stores(bm, 1, 2, 128, npad, I, range(0, I, 128))
     assert np.array_equal(offs, _frag_index(rows, cols, I)), "act offsets follow the fragment layout"
     assert np.array_equal(np.sort(offs), np.arange(npad * I)), "every act element of the real blocks once"
