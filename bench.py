@@ -139,12 +139,12 @@ def kernel_label(kind: str, block_m: int) -> str:
     if kind == "gate_up":
         return {16: "grouped_gemm_skinny_kernel<true,1,2,8,false>", 32: "grouped_gemm_kernel<GemmCfg<32,128,true>,false>",
                 64: "grouped_gemm_wide_kernel<WideCfg<true,64,4,2,1,128,2>,false,false,1>",
-                128: "grouped_gemm_wide_kernel<WideCfg<true,128,4,4,2,128>,false,false,1>",
-                256: "grouped_gemm_wide_kernel<WideCfg<true,128,4,4,2,128>,false,false,2>"}[block_m]
+                128: "grouped_gemm_wide_kernel<WideCfg<true,128,4,4,2,128,1>,false,false,1>",
+                256: "grouped_gemm_wide_kernel<WideCfg<true,128,4,4,2,128,1>,false,false,2>"}[block_m]
     return {16: "grouped_gemm_skinny_kernel<false,4,4,4,true>", 32: "grouped_gemm_kernel<GemmCfg<32,128,false>,true>",
             64: "grouped_gemm_wide_kernel<WideCfg<false,64,4,2,1,128,2>,true,false,1>",
-            128: "grouped_gemm_wide_kernel<WideCfg<false,128,4,4,2,128>,true,true,1>",
-            256: "grouped_gemm_wide_kernel<WideCfg<false,128,4,4,2,128>,true,true,2>"}[block_m]
+            128: "grouped_gemm_wide_kernel<WideCfg<false,128,4,4,2,128,1>,true,true,1>",
+            256: "grouped_gemm_wide_kernel<WideCfg<false,128,4,4,2,128,1>,true,true,2>"}[block_m]
 
 
 def host_cpu_model() -> str:
