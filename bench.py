@@ -267,18 +267,32 @@ def measure_layer(workload: str, steps: int, warmup: int, seed: int, weights: We
     sp = stream.cuda_stream
 
     dense = workload == "dense"
+    g = b  # the down projection's grouping
+    down_bm = block_m
     if dense:
         ids0 = torch.zeros((T, 1), dtype=torch.int32, device="cuda")
         ones = torch.ones((T, 1), dtype=torch.float32, device="cuda")
+        # as gated_mlp: with one expert the down projection may take finer row
+        # blocks (the grouping is the identity at every block size)
+        down_bm = moe.dense_down_block_m(T, H, block_m, torch.cuda.get_device_properties(0).multi_processor_count)
+        if down_bm != block_m:
+            g = moe.allocate(T, H, E, k, I, "cuda", down_bm)
+
+    def align(w13, w2):
+        moe.moe_align_by_expert(ids0 if dense else b.topk_ids, T, k, E, block_m, b.sorted_ids, b.block_expert,
+                                b.expert_counts, b.num_padded, b.workspace, sp)
+        if g is not b:
+            moe.moe_align_by_expert(ids0, T, k, E, down_bm, g.sorted_ids, g.block_expert, g.expert_counts,
+                                    g.num_padded, g.workspace, sp)
+
     calls = [
         lambda w13, w2: None if dense else moe.moe_route(x, wr, bias, b.logits, b.topk_ids, b.topk_weights, T, H, E,
                                                          k, shape.norm_topk_prob, sp),
-        lambda w13, w2: moe.moe_align_by_expert(ids0 if dense else b.topk_ids, T, k, E, block_m, b.sorted_ids,
-                                                b.block_expert, b.expert_counts, b.num_padded, b.workspace, sp),
+        align,
         lambda w13, w2: moe.moe_grouped_gemm_gate_up_silu(x, w13, b.sorted_ids, b.block_expert, b.num_padded, T, k,
                                                           H, I, E, block_m, b.cap, b.act, sp),
-        lambda w13, w2: moe.moe_grouped_gemm_down(b.act, w2, b.sorted_ids, b.block_expert, b.num_padded, T, k, H, I,
-                                                  E, block_m, b.cap, b.y, sp),
+        lambda w13, w2: moe.moe_grouped_gemm_down(b.act, w2, g.sorted_ids, g.block_expert, g.num_padded, T, k, H, I,
+                                                  E, down_bm, g.cap, b.y, sp),
         lambda w13, w2: moe.moe_combine(b.y, ones if dense else b.topk_weights, T, k, H, b.out, sp),
     ]
     gu, dn = KERNELS.index("gate_up"), KERNELS.index("down")
@@ -374,7 +388,7 @@ def measure_layer(workload: str, steps: int, warmup: int, seed: int, weights: We
                  "frac": round(achieved / PEAK_BF16_TFLOPS, 4)}
         rec = counter_record(workload, kind)
         r["kernel"] = f"moe_grouped_gemm_{'gate_up_silu' if kind == 'gate_up' else 'down'}: " + \
-            kernel_label(kind, block_m)
+            kernel_label(kind, down_bm if kind == "down" else block_m)
         r["kernel_ms"] = round(kern_ms, 5)
         r["timing"] = (f"HIP events around each of the {steps} launches in a second timed region of {steps} steps "
                        f"({elapsed_marked * 1e3 / steps:.4f} ms/step with the markers)")
@@ -390,7 +404,8 @@ def measure_layer(workload: str, steps: int, warmup: int, seed: int, weights: We
         "workload": WORKLOAD_TEXT[workload],
         "name": workload,
         "T": T, "hidden": H, "experts": E, "top_k": k, "intermediate": I, "norm_topk_prob": shape.norm_topk_prob,
-        "block_m": block_m, "weight_copies_rotated": copies, "touched_experts": work["touched_experts"],
+        "block_m": block_m, "down_block_m": down_bm, "weight_copies_rotated": copies,
+        "touched_experts": work["touched_experts"],
         "steps": steps, "warmup": warmup,
         "ms_per_step": round(ms_per_step, 5),
         "tokens_per_s": round(T / layer_s, 1),
@@ -409,7 +424,7 @@ def measure_layer(workload: str, steps: int, warmup: int, seed: int, weights: We
             "note": "down projection and weighted combine as one launch (moe_grouped_gemm_down_combine), "
                     f"{steps} steps timed like ms_per_step"},
     }
-    del packed, w13s, w2s, b, x, wr
+    del packed, w13s, w2s, b, g, x, wr
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
     return record, inp

@@ -44,6 +44,7 @@ from .layer import (  # noqa: F401
     PackedExperts,
     allocate,
     check_buffers,
+    dense_down_block_m,
     gated_mlp,
     moe_layer,
     moe_layer_with_norm,

@@ -226,6 +226,20 @@ def moe_layer_with_norm(x: torch.Tensor, residual: Optional[torch.Tensor], norm_
     return b.out, res_out, h
 
 
+def dense_down_block_m(T: int, H: int, block_m: int, cus: int) -> int:
+    """Row-block size of the down projection in the single-expert path.
+
+    With one expert the grouping is the identity at every block size (row r
+    of the sorted order is token r, the pad rows follow), so the two
+    projections may use different row blocks. The down projection's N = H is
+    narrow: when its 128-row tiles (512 columns wide) would not give every
+    compute unit one, 64-row blocks (64x256 tiles, two per CU) are used
+    instead (T = 4096, H = 1024: 66 -> 37 us, gate/up staying at 128 rows)."""
+    if block_m >= 128 and -(-T // 128) * -(-H // 512) < cus:
+        return 64
+    return block_m
+
+
 def gated_mlp(x: torch.Tensor, packed: PackedExperts, *, block_m: Optional[int] = None, out_dtype=torch.bfloat16,
               y_dtype=torch.float16, stream=None) -> torch.Tensor:
     """Dense SwiGLU GatedMLP (down(silu(gate(x)) * up(x)), the "Models and
@@ -247,7 +261,24 @@ def gated_mlp(x: torch.Tensor, packed: PackedExperts, *, block_m: Optional[int] 
                              b.workspace, s)
     _lib.moe_grouped_gemm_gate_up_silu(x, packed.w13, b.sorted_ids, b.block_expert, b.num_padded, T, 1, H, I, 1,
                                        b.block_m, b.cap, b.act, s)
-    _lib.moe_grouped_gemm_down(b.act, packed.w2, b.sorted_ids, b.block_expert, b.num_padded, T, 1, H, I, 1,
-                               b.block_m, b.cap, b.y, s)
+    cus = torch.cuda.get_device_properties(x.device).multi_processor_count if x.is_cuda else 0
+    down_bm = b.block_m if block_m is not None else dense_down_block_m(T, H, b.block_m, cus)
+    if down_bm == b.block_m:
+        _lib.moe_grouped_gemm_down(b.act, packed.w2, b.sorted_ids, b.block_expert, b.num_padded, T, 1, H, I, 1,
+                                   b.block_m, b.cap, b.y, s)
+    else:
+        # the grouping at the finer block size (the identity again), from the
+        # library's own grouping call; act's rows are the same rows and hold
+        # at least that grouping's capacity
+        cap = _lib.moe_align_capacity(T, 1, 1, down_bm)
+        assert cap <= b.cap and b.cap % down_bm == 0
+        i32 = dict(dtype=torch.int32, device=x.device)
+        sorted_ids, block_expert = torch.empty((cap,), **i32), torch.empty((cap // down_bm,), **i32)
+        counts, num_padded = torch.empty((1,), **i32), torch.empty((1,), **i32)
+        ws_bytes = _lib.moe_align_workspace_bytes(T, 1, 1, down_bm)
+        ws = torch.empty((ws_bytes,), dtype=torch.uint8, device=x.device) if ws_bytes else None
+        _lib.moe_align_by_expert(ids, T, 1, 1, down_bm, sorted_ids, block_expert, counts, num_padded, ws, s)
+        _lib.moe_grouped_gemm_down(b.act, packed.w2, sorted_ids, block_expert, num_padded, T, 1, H, I, 1, down_bm,
+                                   cap, b.y, s)
     _lib.moe_combine(b.y, ones, T, 1, H, b.out, s)
     return b.out

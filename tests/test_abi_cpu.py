@@ -50,6 +50,11 @@ def test_capacity_and_workspace():
     for T, bm in picks.items():
         assert moe.moe_pick_block_m(T, 8, 128) == bm, T
     assert moe.moe_pick_block_m(-1, 8, 128) == -1 and moe.moe_pick_block_m(4, 0, 8) == -1
+    # single-expert path: 64-row down blocks only while 128-row tiles would
+    # leave compute units idle
+    assert moe.dense_down_block_m(4096, 1024, 128, 256) == 64
+    assert moe.dense_down_block_m(65536, 1024, 128, 256) == 128
+    assert moe.dense_down_block_m(4096, 1024, 16, 256) == 16
 
 
 def _raw():

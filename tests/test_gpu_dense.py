@@ -51,3 +51,19 @@ def test_dense_mlp_equals_moe_layer_with_one_expert():
         b = moe.moe_layer(bf16_tensor(x), wr, top_k=1, packed=packed, block_m=bm)
         torch.cuda.synchronize()
         assert np.array_equal(to_bits(a), to_bits(b))
+
+
+@pytest.mark.parametrize("T,H,I", [(1000, 1024, 3072), (4096, 1024, 3072), (129, 512, 256)])
+def test_dense_finer_down_blocks_same_bits(T, H, I):
+    """With the block size left to the library the down projection of a
+    narrow layer runs on 64-row blocks (its own grouping, the identity
+    again) while gate/up keeps 128-row blocks: the same MFMA shape and k
+    order per element, so the output equals the all-128-row run bit for bit."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert moe.dense_down_block_m(T, H, moe.moe_pick_block_m(T, 1, 1), cus) == 64
+    x, w13, w2 = _dense_inputs(T, H, I, seed=T + 1)
+    packed = moe.pack_experts(bf16_tensor(w13), bf16_tensor(w2))
+    auto = moe.gated_mlp(bf16_tensor(x), packed)
+    fixed = moe.gated_mlp(bf16_tensor(x), packed, block_m=128)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_bits(auto), to_bits(fixed))
