@@ -16,7 +16,9 @@
 // positions follow flat-index order exactly. Each workgroup also writes the
 // sentinel into the pad rows and the block owners of its share of the
 // capacity. When all pairs fit one tile, kernel 2 counts them itself and
-// kernel 1 is skipped.
+// kernel 1 is skipped; up to kAlignFusedMaxPairs pairs (ids 16-byte
+// aligned) every workgroup of kernel 2 counts all pairs itself, the earlier
+// tiles' separately, and kernel 1 is skipped as well.
 #include <mutex>
 
 #include "abi_util.h"
@@ -98,7 +100,8 @@ __global__ __launch_bounds__(kAlignThreads) void align_scatter_kernel(
     int my[PT];
     load_tile_ids<PT>(ids, n, E, tile, my);
 
-    if (fused_hist) {
+    if (fused_hist == 1) {
+        // the only tile: its own pairs are all pairs
         for (int e = tid; e < kMaxExperts; e += blockDim.x) total[e] = 0;
         __syncthreads();
 #pragma unroll
@@ -106,6 +109,40 @@ __global__ __launch_bounds__(kAlignThreads) void align_scatter_kernel(
             if (my[q] >= 0) atomicAdd(&total[my[q]], 1);
         __syncthreads();
         if (tid < E) base[tid] = 0;
+    } else if (fused_hist == 2) {
+        // every workgroup counts all n pairs itself (16-byte loads, ids
+        // 16-byte aligned), and separately those of the earlier tiles: no
+        // histogram kernel and no workspace round trip
+        for (int e = tid; e < kMaxExperts; e += blockDim.x) {
+            total[e] = 0;
+            base[e] = 0;
+        }
+        __syncthreads();
+        auto count = [&](int64_t i, int e) {
+            if ((unsigned)e < (unsigned)E) {
+                atomicAdd(&total[e], 1);
+                if (i < start) atomicAdd(&base[e], 1);
+            }
+        };
+        const int64_t n4 = n / 4;
+        constexpr int B = 16;  // 16-byte loads in flight per thread
+        for (int64_t v0 = tid; v0 < n4; v0 += (int64_t)B * kAlignThreads) {
+            int4 q[B];
+#pragma unroll
+            for (int u = 0; u < B; ++u) q[u] = ((const int4*)ids)[min(v0 + (int64_t)u * kAlignThreads, n4 - 1)];
+#pragma unroll
+            for (int u = 0; u < B; ++u) {
+                const int64_t v = v0 + (int64_t)u * kAlignThreads;
+                if (v < n4) {
+                    count(4 * v, q[u].x);
+                    count(4 * v + 1, q[u].y);
+                    count(4 * v + 2, q[u].z);
+                    count(4 * v + 3, q[u].w);
+                }
+            }
+        }
+        for (int64_t i = 4 * n4 + tid; i < n; i += kAlignThreads) count(i, ids[i]);
+        __syncthreads();
     } else if (tid < E) {
         // every tile's count of expert tid, 32 loads in flight at a time
         int tot = 0, pre = 0;
@@ -208,15 +245,23 @@ static int64_t align_ntiles(int64_t T, int32_t k) {
     return (T * k + ts - 1) / ts;
 }
 
+// Up to this many pairs (and with 16-byte aligned ids) every workgroup of
+// the scatter kernel counts all pairs itself instead of reading the
+// histogram kernel's per-tile counts: one launch and no workspace round
+// trip. Grouping step (events) at 4096 pairs: 14.4 -> 11.5 us; at 32768
+// pairs each of the 32 workgroups reading all ids made it slower (17.3 ->
+// 20.9 us), so larger groupings keep the histogram kernel.
+constexpr int64_t kAlignFusedMaxPairs = 8192;
+
 template <int PT>
 static void launch_align(const int32_t* ids, int64_t n, int E, int BM, int64_t cap, int64_t ntiles, int32_t* ws,
                          int32_t* sorted_ids, int32_t* block_expert, int32_t* counts, int32_t* num_padded,
                          hipStream_t s) {
-    if (ntiles > 1)
+    const int fused = ntiles <= 1 ? 1 : (n <= kAlignFusedMaxPairs && ((uintptr_t)ids & 15) == 0) ? 2 : 0;
+    if (!fused)
         hipLaunchKernelGGL(align_hist_kernel<PT>, dim3((unsigned)ntiles), dim3(kAlignThreads), 0, s, ids, n, E, ws);
     hipLaunchKernelGGL(align_scatter_kernel<PT>, dim3((unsigned)ntiles), dim3(kAlignThreads), 0, s, ids, n, E, BM, cap,
-                       (int)ntiles, (const int32_t*)ws, (int)(ntiles <= 1), sorted_ids, block_expert, counts,
-                       num_padded);
+                       (int)ntiles, (const int32_t*)ws, fused, sorted_ids, block_expert, counts, num_padded);
 }
 
 // Workspace of moe_align_by_expert_noalloc: the per-tile histograms live in

@@ -144,10 +144,15 @@ def test_route_special_logits_rank_order():
 # ----------------------------------------------------------------------------
 # Expert-grouped permutation
 # ----------------------------------------------------------------------------
-def _align_gpu(ids_np, E, bm):
+def _align_gpu(ids_np, E, bm, offset=0):
+    """offset: pass the ids as a view that starts ``offset`` int32s into its
+    allocation (offset 1: not 16-byte aligned)."""
     T, k = ids_np.shape
     cap = moe.moe_align_capacity(T, k, E, bm)
-    ids = torch.from_numpy(np.ascontiguousarray(ids_np, dtype=np.int32)).cuda()
+    flat = torch.from_numpy(np.ascontiguousarray(ids_np, dtype=np.int32).reshape(-1))
+    buf = torch.zeros((offset + T * k,), dtype=torch.int32, device="cuda")
+    buf[offset:] = flat.cuda()
+    ids = buf[offset:].view(T, k)
     sorted_ids = torch.full((cap,), -7, dtype=torch.int32, device="cuda")
     block_expert = torch.full((cap // bm,), -7, dtype=torch.int32, device="cuda")
     counts = torch.empty((E,), dtype=torch.int32, device="cuda")
@@ -159,8 +164,8 @@ def _align_gpu(ids_np, E, bm):
     return sorted_ids.cpu().numpy(), block_expert.cpu().numpy(), counts.cpu().numpy(), int(npad.item())
 
 
-def _check_align(ids_np, E, bm):
-    g = _align_gpu(ids_np, E, bm)
+def _check_align(ids_np, E, bm, offset=0):
+    g = _align_gpu(ids_np, E, bm, offset)
     o = oracle.align(ids_np, E, bm)
     assert np.array_equal(g[0], o[0]), "sorted_ids"
     assert np.array_equal(g[1], o[1]), "block_expert"
@@ -193,6 +198,20 @@ def test_align_bitexact_edge_shapes(T, k, E, bm):
     ids = np.stack([rng.choice(E, size=k, replace=False, p=p) if np.count_nonzero(p) >= k
                     else rng.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32)
     _check_align(ids, E, bm)
+
+
+@pytest.mark.parametrize("T,k,E,bm", [(4097, 1, 3, 32), (513, 8, 128, 64), (1024, 8, 128, 128), (1, 8, 128, 16),
+                                      (4096, 8, 128, 128)])
+@pytest.mark.parametrize("offset", [0, 1])
+def test_align_bitexact_aligned_and_unaligned_ids(T, k, E, bm, offset):
+    """Up to 8192 pairs the grouping counts all pairs inside its scatter
+    kernel with 16-byte loads when the ids are 16-byte aligned, and takes
+    the two-kernel path (histogram kernel + workspace) when they are not or
+    when there are more pairs: all give the oracle's grouping, ragged pair
+    counts included."""
+    rng = np.random.default_rng(T * 7 + k)
+    ids = np.stack([rng.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32)
+    _check_align(ids, E, bm, offset)
 
 
 # ----------------------------------------------------------------------------
